@@ -1,0 +1,217 @@
+"""Benchmark: one CP rank's share of context-parallel causal attention.
+
+One step = rank 0's share of the 131072-token zigzag workload (CP=8,
+MLA-prefill shape: 128 heads, qk 192, v 128, bf16) on the ring (pass-KV)
+path: the shard plan, eight partial attention launches against each rank's
+zigzag KV pair (masked by absolute key positions), and the LSE merge of the
+eight partials.  Inputs are seeded synthetic N(0,1) tensors already resident
+in HBM; the KV pairs a ring would receive are built before timing.
+
+Prints ONE JSON line.  ``value`` is useful causal TFLOP/s of the step
+(visible (q,k) pairs x heads x 2 x (192 + 128) / step time).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "causal attn TFLOP/s per CP-rank shard + % bf16 MFMA peak; merge GB/s % HBM"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--rank", type=int, default=0, help="CP rank whose share is timed")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    return ap.parse_args()
+
+
+def _useful_flops(pairs_per_head, hq, dqk, dv):
+    return float(pairs_per_head) * hq * 2.0 * (dqk + dv)
+
+
+def _rank_pairs(plan):
+    return int(sum(int(p) + 1 for p in plan.positions))
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: every CP rank's share is a separate launch on "
+              f"that GPU, so --gpus {a.gpus} is not a configuration this build measures.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import context_causal_attention_cp_amd as cp
+    import workloads
+
+    dev = "cuda"
+    w = workloads.get("zigzag_t131072_mla")
+    C, r = w.cp_size, a.rank
+    lens, pre = list(w.new_lens), list(w.prefix_lens)
+    q, k, v = workloads.prefill_tensors(w, dev)
+    plan = cp.shard_plan("zigzag", C, r, lens, pre)
+    q_loc = q.index_select(0, torch.from_numpy(plan.global_idx.astype(np.int64)).to(dev))
+    kv = []
+    for j in range(C):
+        idx = torch.from_numpy(cp.shard_plan("zigzag", C, j, lens, pre).global_idx
+                               .astype(np.int64)).to(dev)
+        kv.append((k.index_select(0, idx), v.index_select(0, idx), idx.to(torch.int32)))
+    n = plan.num_local
+    o_parts = torch.empty((C, n, w.hq, w.dv), device=dev, dtype=torch.bfloat16)
+    l_parts = torch.empty((C, n, w.hq), device=dev, dtype=torch.float32)
+    o_out = torch.empty((n, w.hq, w.dv), device=dev, dtype=torch.bfloat16)
+    l_out = torch.empty((n, w.hq), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * C + 2)] for _ in range(a.steps)]
+
+    def step(events=None):
+        pl = cp.shard_plan("zigzag", C, r, lens, pre)
+        for j in range(C):
+            kj, vj, pj = kv[j]
+            segs = [cp.Segment(s.req, s.q_begin, s.q_end, s.pos_begin, s.pos_stride, 0,
+                               kj.shape[0]) for s in pl.segments]
+            if events:
+                events[2 * j].record(stream)
+            cp.attn_fwd(q_loc, kj, vj, segs, w.scale, kv_pos=pj, o=o_parts[j], lse=l_parts[j])
+            if events:
+                events[2 * j + 1].record(stream)
+        if events:
+            events[2 * C].record(stream)
+        cp.lse_merge(o_parts, l_parts, o_out=o_out, lse_out=l_out)
+        if events:
+            events[2 * C + 1].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / a.steps
+
+    pairs = _rank_pairs(plan)
+    flops = _useful_flops(pairs, w.hq, w.dqk, w.dv)
+    attn_ms = [sum(ev[i][2 * j].elapsed_time(ev[i][2 * j + 1]) for j in range(C))
+               for i in range(a.steps)]
+    merge_ms = [ev[i][2 * C].elapsed_time(ev[i][2 * C + 1]) for i in range(a.steps)]
+    attn_ms_avg = float(np.mean(attn_ms))
+    merge_ms_avg = float(np.mean(merge_ms))
+    attn_launch_ms = attn_ms_avg / C
+    achieved_tflops = flops / (attn_ms_avg * 1e-3) / 1e12
+
+    # merge algorithmic bytes: live partial rows' O (bf16) + every LSE + outputs
+    lp = l_parts.isfinite()
+    live_rows = int(lp.sum().item())                   # (row, head, part) triples
+    merge_bytes = (live_rows * w.dv * 2 + C * n * w.hq * 4 + n * w.hq * (w.dv * 2 + 4))
+    merge_gbs = merge_bytes / (merge_ms_avg * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 Q/K/V",
+        "config": {
+            "workload": "zigzag_t131072_mla rank %d: plan + 8 ring partials + LSE merge" % r,
+            "strategy": "zigzag", "cp_size": C, "cp_rank": r, "new_tokens": w.total_new,
+            "local_rows": n, "heads_q": w.hq, "heads_kv": w.hkv, "dqk": w.dqk, "dv": w.dv,
+            "visible_pairs_per_head": pairs, "useful_tflop_per_step": round(flops / 1e12, 3),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16_kernel<192,128>",
+            "achieved": round(achieved_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(attn_launch_ms, 4),
+        },
+        "merge": {
+            "kernel": "lse_merge_kernel<bf16,bf16>",
+            "ms": round(merge_ms_avg, 4),
+            "algorithmic_bytes": merge_bytes,
+            "GB/s": round(merge_gbs, 1),
+            "frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4),
+        },
+    }
+    del kv
+    torch.cuda.empty_cache()
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(w, q, k, v, plan, a.cpu_baseline_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def _cpu_baseline(w, q, k, v, plan, budget_s):
+    """The oracle as it stands, timed on the host: dense attention of a
+    sample of rank 0's rows for as many heads as fit the time budget;
+    reported as useful TFLOP/s of the rows it computed."""
+    import numpy as np
+    import torch
+    from oracle import attn_oracle as ao
+    from oracle import index_oracle as ix
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    segs = ix.segments("zigzag", w.cp_size, 0, list(w.new_lens), list(w.prefix_lens))
+    rng = np.random.default_rng(99)
+    rows = sorted(set(int(x) for x in rng.choice(plan.num_local, size=16, replace=False)))
+    q_loc = q.index_select(0, torch.from_numpy(plan.global_idx.astype(np.int64)).to(q.device))
+    q_rows = q_loc[torch.tensor(rows, device=q.device)]
+    pos = plan.positions[rows].astype(np.int64)
+    pairs_per_head = int(np.sum(pos + 1))
+    done_heads = 0
+    t_compute = 0.0
+    t_start = time.perf_counter()
+    for h in range(w.hq):
+        qh = q_rows[:, h].float().cpu().numpy()
+        kh = k[:, h].float().cpu().numpy()
+        vh = v[:, h].float().cpu().numpy()
+        sub = [ix.Segment(0, i, i + 1, int(pos[i]), 1, 0, int(pos[i]) + 1) for i in range(len(rows))]
+        t0 = time.perf_counter()
+        ao.shard_attention(qh[:, None], kh[:, None], vh[:, None], sub, 1, 1, w.scale)
+        t_compute += time.perf_counter() - t0
+        done_heads += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    flops = _useful_flops(pairs_per_head, done_heads, w.dqk, w.dv)
+    return {
+        "value": round(flops / t_compute / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rows)} seeded rows of rank 0 x {done_heads} of {w.hq} heads, dense "
+                  f"causal fp64 over up to {int(pos.max()) + 1} keys "
+                  f"({flops / 1e9:.1f} GFLOP in {t_compute:.1f} s)",
+    }
+
+
+if __name__ == "__main__":
+    main()

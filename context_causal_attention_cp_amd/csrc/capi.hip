@@ -1,0 +1,251 @@
+// C ABI: argument checks, launch planning and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdio>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "cp_attn.h"
+#include "internal.h"
+
+using namespace cpattn;
+
+namespace {
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+enum class Path { None, Bf16Mfma, F32 };
+
+Path pick_path(const cp_attn_args &a) {
+  if (a.dtype == CP_BF16) {
+    if ((a.dqk == 128 && a.dv == 128) || (a.dqk == 192 && a.dv == 128) ||
+        (a.dqk == 64 && a.dv == 64))
+      return Path::Bf16Mfma;
+    return Path::None;
+  }
+  if (a.dtype == CP_F32) {
+    if (a.dqk == a.dv && (a.dqk == 64 || a.dqk == 128)) return Path::F32;
+    return Path::None;
+  }
+  return Path::None;
+}
+
+cp_status check_attn(const cp_attn_args *a) {
+  if (!a) return CP_ERR_ARG;
+  if (a->dtype != CP_BF16 && a->dtype != CP_F32) return CP_ERR_UNSUPPORTED;
+  if (a->o_dtype != CP_BF16 && a->o_dtype != CP_F32) return CP_ERR_UNSUPPORTED;
+  if (a->num_q_rows < 0 || a->num_kv_rows < 0 || a->num_segs < 0) return CP_ERR_ARG;
+  if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv != 0) return CP_ERR_ARG;
+  if (a->dqk < 1 || a->dv < 1) return CP_ERR_ARG;
+  if (!std::isfinite(a->scale)) return CP_ERR_ARG;
+  if (a->num_segs > 0 && !a->segs) return CP_ERR_ARG;
+  for (int32_t i = 0; i < a->num_segs; ++i) {
+    const cp_segment &s = a->segs[i];
+    if (s.q_begin < 0 || s.q_end < s.q_begin || s.q_end > a->num_q_rows) return CP_ERR_ARG;
+    if (s.kv_begin < 0 || s.kv_end < s.kv_begin || s.kv_end > a->num_kv_rows) return CP_ERR_ARG;
+    if (s.pos_stride < 0) return CP_ERR_ARG;
+    // every row position must fit int32 with room for the kernels' sentinels
+    const int64_t n = s.q_end - s.q_begin;
+    if (n > 0) {
+      const int64_t last = static_cast<int64_t>(s.pos_begin) + (n - 1) * s.pos_stride;
+      if (s.pos_begin < -(1 << 29) || last > (INT32_MAX >> 1)) return CP_ERR_ARG;
+    }
+  }
+  if (pick_path(*a) == Path::None) return CP_ERR_UNSUPPORTED;
+  return CP_OK;
+}
+
+cp_status check_attn_buffers(const cp_attn_args *a) {
+  const bool any_rows = a->num_segs > 0;
+  if (!any_rows) return CP_OK;
+  if (!a->q || !a->k || !a->v || !a->o || !a->lse) return CP_ERR_ARG;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return CP_ERR_ARG;
+  const int64_t in_vec = a->dtype == CP_BF16 ? 8 : 4;
+  const int64_t out_vec = a->o_dtype == CP_BF16 ? 8 : 4;
+  const int64_t s_in[6] = {a->q_row_stride, a->q_head_stride, a->k_row_stride,
+                           a->k_head_stride, a->v_row_stride, a->v_head_stride};
+  for (int64_t s : s_in)
+    if (s < 0 || s % in_vec != 0) return CP_ERR_ARG;
+  if (a->o_row_stride < 0 || a->o_head_stride < 0 || a->o_row_stride % out_vec != 0 ||
+      a->o_head_stride % out_vec != 0)
+    return CP_ERR_ARG;
+  if (a->lse_row_stride < a->hq && a->num_q_rows > 1) return CP_ERR_ARG;
+  return CP_OK;
+}
+
+AttnParams make_params(const cp_attn_args &a) {
+  AttnParams p{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.kv_pos = a.kv_pos;
+  p.q_rs = a.q_row_stride;
+  p.q_hs = a.q_head_stride;
+  p.k_rs = a.k_row_stride;
+  p.k_hs = a.k_head_stride;
+  p.v_rs = a.v_row_stride;
+  p.v_hs = a.v_head_stride;
+  p.o_rs = a.o_row_stride;
+  p.o_hs = a.o_head_stride;
+  p.lse_rs = a.lse_row_stride;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.causal = a.causal ? 1 : 0;
+  p.o_bf16 = a.o_dtype == CP_BF16;
+  p.ws = a.workspace;
+  p.ws_bytes = static_cast<int64_t>(a.workspace_bytes);
+  return p;
+}
+
+// Splits the non-empty segments into launches of at most kMaxLaunchSegs,
+// heaviest first (largest visible KV extent), numbering their tiles.
+std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
+  std::vector<int32_t> order;
+  for (int32_t i = 0; i < a.num_segs; ++i)
+    if (a.segs[i].q_end > a.segs[i].q_begin && a.segs[i].kv_end > a.segs[i].kv_begin)
+      order.push_back(i);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return a.segs[x].kv_end - a.segs[x].kv_begin > a.segs[y].kv_end - a.segs[y].kv_begin;
+  });
+  std::vector<LaunchSegs> out;
+  for (size_t i = 0; i < order.size(); i += kMaxLaunchSegs) {
+    LaunchSegs L{};
+    const size_t n = std::min<size_t>(kMaxLaunchSegs, order.size() - i);
+    int32_t tiles = 0;
+    for (size_t j = 0; j < n; ++j) {
+      const cp_segment &s = a.segs[order[i + j]];
+      SegDesc &d = L.s[j];
+      d.q_begin = s.q_begin;
+      d.q_len = s.q_end - s.q_begin;
+      d.pos_begin = s.pos_begin;
+      d.pos_stride = s.pos_stride;
+      d.kv_begin = s.kv_begin;
+      d.kv_len = s.kv_end - s.kv_begin;
+      d.tile_begin = tiles;
+      tiles += (d.q_len + tile_rows - 1) / tile_rows;
+    }
+    L.num_segs = static_cast<int32_t>(n);
+    L.num_tiles = tiles;
+    out.push_back(L);
+  }
+  return out;
+}
+
+// Rows that no kernel writes because their segment sees no KV row at all
+// (kv_end == kv_begin) still get O = 0, LSE = -inf: handled by a tiny fill.
+__global__ void fill_empty_rows(float *lse, int64_t lse_rs, void *o, int64_t o_rs,
+                                int64_t o_hs, int o_bf16, int hq, int dv, int q_begin,
+                                int q_len) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = (int64_t)hq * dv;
+  if (e >= per_row * q_len) return;
+  const int64_t r = q_begin + e / per_row;
+  const int h = (int)((e % per_row) / dv), d = (int)(e % dv);
+  if (o_bf16)
+    ((__bf16 *)o)[r * o_rs + h * o_hs + d] = (__bf16)0.f;
+  else
+    ((float *)o)[r * o_rs + h * o_hs + d] = 0.f;
+  if (d == 0) lse[r * lse_rs + h] = -INFINITY;
+}
+
+}  // namespace
+
+extern "C" const char *cp_status_str(int32_t s) {
+  switch (s) {
+    case CP_OK: return "CP_OK";
+    case CP_ERR_ARG: return "CP_ERR_ARG: invalid argument";
+    case CP_ERR_UNSUPPORTED: return "CP_ERR_UNSUPPORTED: no kernel for this dtype/shape";
+    case CP_ERR_SMALL_BUFFER: return "CP_ERR_SMALL_BUFFER: output capacity too small";
+    case CP_ERR_DEVICE: return "CP_ERR_DEVICE: HIP launch error";
+    default: return "unknown cp_status";
+  }
+}
+
+extern "C" const char *cp_version(void) { return "0.1.0"; }
+
+namespace {
+thread_local char g_last_error[256] = "";
+}  // namespace
+
+namespace cpattn {
+cp_status device_error(hipError_t e) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return CP_ERR_DEVICE;
+}
+}  // namespace cpattn
+
+extern "C" const char *cp_last_error(void) { return g_last_error; }
+
+extern "C" cp_status cp_attn_workspace_size(const cp_attn_args *a, size_t *bytes) {
+  cp_status st = check_attn(a);
+  if (st != CP_OK) return st;
+  if (!bytes) return CP_ERR_ARG;
+  *bytes = 0;
+  return CP_OK;
+}
+
+extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
+  cp_status st = check_attn(a);
+  if (st != CP_OK) return st;
+  st = check_attn_buffers(a);
+  if (st != CP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const AttnParams p = make_params(*a);
+  const Path path = pick_path(*a);
+  const int tile_rows = path == Path::F32 ? attn_f32_tile_rows(a->dqk)
+                                          : attn_bf16_tile_rows(a->dqk, a->dv);
+  (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
+  for (const LaunchSegs &L : plan_launches(*a, tile_rows)) {
+    hipError_t e = path == Path::F32 ? launch_attn_f32(p, L, a->dqk, s)
+                                     : launch_attn_bf16(p, L, a->dqk, a->dv, s);
+    if (e != hipSuccess) return device_error(e);
+  }
+  for (int32_t i = 0; i < a->num_segs; ++i) {
+    const cp_segment &g = a->segs[i];
+    const int32_t n = g.q_end - g.q_begin;
+    if (n > 0 && g.kv_end == g.kv_begin) {
+      const int64_t elems = static_cast<int64_t>(n) * a->hq * a->dv;
+      hipLaunchKernelGGL(fill_empty_rows, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0,
+                         s, a->lse, a->lse_row_stride, a->o, a->o_row_stride,
+                         a->o_head_stride, a->o_dtype == CP_BF16 ? 1 : 0, a->hq, a->dv,
+                         g.q_begin, n);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return device_error(e);
+    }
+  }
+  return CP_OK;
+}
+
+extern "C" cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads,
+                                  int32_t dv, const void *o_parts, int32_t part_dtype,
+                                  int64_t o_part_stride, const float *lse_parts,
+                                  int64_t lse_part_stride, void *o_out, int32_t out_dtype,
+                                  float *lse_out, void *stream) {
+  if ((part_dtype != CP_BF16 && part_dtype != CP_F32) ||
+      (out_dtype != CP_BF16 && out_dtype != CP_F32))
+    return CP_ERR_UNSUPPORTED;
+  if (num_parts < 1 || rows < 0 || heads < 0 || dv < 8 || dv % 8 != 0) return CP_ERR_ARG;
+  // dv/8 lanes per (row, head) must tile a 256-lane workgroup
+  const int32_t lanes = dv / 8;
+  if (lanes > 256 || (lanes & (lanes - 1)) != 0) return CP_ERR_ARG;
+  const int64_t pairs = static_cast<int64_t>(rows) * heads;
+  if (pairs == 0) return CP_OK;
+  if (!o_parts || !lse_parts || !o_out) return CP_ERR_ARG;
+  if (!aligned16(o_parts) || !aligned16(o_out)) return CP_ERR_ARG;
+  if (o_part_stride < pairs * dv && num_parts > 1) return CP_ERR_ARG;
+  if (lse_part_stride < pairs && num_parts > 1) return CP_ERR_ARG;
+  if (o_part_stride % 8 != 0 || o_part_stride < 0 || lse_part_stride < 0) return CP_ERR_ARG;
+  (void)hipGetLastError();
+  hipError_t e = launch_lse_merge(num_parts, pairs, dv, o_parts, part_dtype == CP_BF16,
+                                  o_part_stride, lse_parts, lse_part_stride, o_out,
+                                  out_dtype == CP_BF16, lse_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CP_OK : device_error(e);
+}

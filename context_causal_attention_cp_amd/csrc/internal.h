@@ -1,0 +1,78 @@
+// Internal launch descriptors shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "cp_attn.h"
+
+namespace cpattn {
+
+// MI355X: 256 compute units in 8 XCDs; consecutive workgroup ids are dealt
+// round-robin over the XCDs, each of which has its own L2.
+constexpr int kNumXcd = 8;
+
+// Segments per launch travel in the kernel arguments.
+constexpr int kMaxLaunchSegs = 64;
+
+// One segment as a kernel sees it.  Tiles of a launch are numbered heaviest
+// first: segments in descending kv_len, and inside a segment from its last
+// q tile (longest causal extent) to its first.
+struct SegDesc {
+  int32_t q_begin;     // first local row
+  int32_t q_len;       // rows
+  int32_t pos_begin;   // position of the first row
+  int32_t pos_stride;  // position step per row
+  int32_t kv_begin;    // first KV row
+  int32_t kv_len;      // KV rows visible at most
+  int32_t tile_begin;  // first launch tile number of this segment
+  int32_t reserved;
+};
+
+struct LaunchSegs {
+  int32_t num_segs;
+  int32_t num_tiles;   // tiles over all segments of this launch
+  SegDesc s[kMaxLaunchSegs];
+};
+
+struct AttnParams {
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;
+  float *lse;
+  const int32_t *kv_pos;  // null: position = kv row - kv_begin
+  int64_t q_rs, q_hs;
+  int64_t k_rs, k_hs;
+  int64_t v_rs, v_hs;
+  int64_t o_rs, o_hs;
+  int64_t lse_rs;
+  int32_t hq, hkv;
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+  int32_t causal;
+  int32_t o_bf16;     // 1: o is bf16, 0: fp32
+  void *ws;           // workspace (device)
+  int64_t ws_bytes;
+};
+
+// Records the HIP error for cp_last_error and returns CP_ERR_DEVICE.
+cp_status device_error(hipError_t e);
+
+// Kernel entry points (one translation unit each).  They enqueue on
+// `stream` and return the launch status.
+hipError_t launch_attn_bf16(const AttnParams &p, const LaunchSegs &L, int dqk,
+                            int dv, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams &p, const LaunchSegs &L, int d,
+                           hipStream_t stream);
+int attn_bf16_tile_rows(int dqk, int dv);
+int attn_f32_tile_rows(int d);
+
+hipError_t launch_lse_merge(int32_t parts, int64_t pairs, int32_t dv,
+                            const void *o_parts, int part_bf16,
+                            int64_t o_part_stride, const float *lse_parts,
+                            int64_t lse_part_stride, void *o_out, int out_bf16,
+                            float *lse_out, hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,234 @@
+/*
+ * cp_attn.h -- C ABI of libcpattn: the per-rank hot path of context-parallel
+ * causal attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operations, and where the pages define them:
+ *
+ *   cp_shard_plan     which new tokens a CP rank owns, in what local order,
+ *                     with what positions and causal KV extents.
+ *                     "Prefill Context Parallelism" (SGLang docs), sections
+ *                     "Zigzag strategy" and "Interleave strategy".
+ *   cp_restore_index  the permutation that puts the rank-major all-gathered
+ *                     token order back into causal order.  "What is Context
+ *                     Parallelism" (blog), sections 2.1 and 5.1.
+ *   cp_attn_fwd       causal attention of one rank's query rows against a KV
+ *                     buffer (the gathered KV, one ring round's KV block, or
+ *                     one decode shard), giving the normalised output O and
+ *                     its log-sum-exp L.  Same blog, sections 2.1, 3.1-3.3;
+ *                     GQA head sharing section 4.1, MLA latent section 4.2.
+ *   cp_lse_merge      merge of partial (O_j, L_j) into the exact result.
+ *                     Same blog, section 3.6.
+ *
+ * Conventions shared by every call:
+ *   - Ownership: the caller owns every buffer (host and device) and the
+ *     stream.  The library keeps no state between calls and allocates no
+ *     device memory; scratch comes from a caller workspace whose size
+ *     cp_attn_workspace_size reports.
+ *   - Errors: every call returns a cp_status and never throws.  Arguments
+ *     are checked on the host before anything is enqueued; on an error
+ *     nothing is enqueued.  CP_ERR_SMALL_BUFFER still writes the required
+ *     sizes to the size outputs.
+ *   - Asynchrony: the GPU calls only enqueue work on `stream` (a hipStream_t
+ *     passed as void*; NULL is the null stream).  The caller synchronises.
+ *   - Determinism: planner outputs are pure functions of the inputs; a GPU
+ *     call with the same inputs is bitwise repeatable.
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CP_OK = 0,
+  CP_ERR_ARG = 1,          /* an argument is out of range or inconsistent  */
+  CP_ERR_UNSUPPORTED = 2,  /* valid, but no kernel for this shape/dtype     */
+  CP_ERR_SMALL_BUFFER = 3, /* an output capacity is too small               */
+  CP_ERR_DEVICE = 4        /* the HIP runtime reported an error at launch   */
+} cp_status;
+
+typedef enum { CP_ZIGZAG = 0, CP_INTERLEAVE = 1 } cp_strategy;
+
+typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
+
+/*
+ * One segment: a run of a rank's local query rows that belong to one request
+ * and whose positions form an arithmetic sequence.  Zigzag gives one segment
+ * per owned non-empty block (early block, then late block, per request);
+ * interleave gives one segment per request the rank owns tokens of.
+ *
+ *   req         request index in the batch
+ *   q_begin     first local row; q_end one past the last
+ *   pos_begin   absolute position of row q_begin (cached prefix included)
+ *   pos_stride  position step between consecutive rows (1 zigzag, C interleave)
+ *   kv_begin    first row of the request in the KV buffer
+ *   kv_end      one past the last KV row the segment can see: the request's
+ *               rows are packed prefix then new tokens, so for the gathered
+ *               KV this is kv_begin + (last row's position) + 1.  This is the
+ *               block's own "kv length" that the zigzag metadata records.
+ */
+typedef struct {
+  int32_t req, q_begin, q_end, pos_begin, pos_stride, kv_begin, kv_end;
+} cp_segment;
+
+/*
+ * cp_shard_plan -- host only, integer.
+ * "Prefill Context Parallelism", "Zigzag strategy": each request's new
+ * tokens are cut into 2C contiguous blocks, the first (T mod 2C) blocks one
+ * token longer; rank r owns blocks r and 2C-1-r; the cut restarts per
+ * request.  "Interleave strategy": rank r owns flattened new-token indices
+ * g = r, r+C, r+2C, ... counted over the whole batch without reset.
+ * Positions keep their original values (prefix_b + offset).
+ *
+ * In:  strategy (cp_strategy), cp_size C >= 1, 0 <= cp_rank < C,
+ *      num_reqs >= 0, new_lens[num_reqs] >= 0, prefix_lens[num_reqs] >= 0
+ *      (prefix_lens may be NULL: all zero).  All host pointers.
+ * Out (each optional, NULL = not wanted):
+ *      segs[seg_cap]          the rank's segments, in local row order
+ *      *num_segs              number of segments
+ *      positions[tok_cap]     absolute position of each local row
+ *      global_idx[tok_cap]    flattened new-token index of each local row
+ *      *num_local             number of local rows N_r
+ *      *padded_local          max over ranks of N_r (the per-rank slice length
+ *                             of the padded, all-gathered buffer)
+ * Errors: CP_ERR_ARG for a bad strategy, C, rank or negative length, or
+ *      int32 overflow of a total; CP_ERR_SMALL_BUFFER when a non-NULL array
+ *      is shorter than needed (the size outputs are still written).
+ */
+cp_status cp_shard_plan(int32_t strategy, int32_t cp_size, int32_t cp_rank,
+                        int32_t num_reqs, const int32_t *new_lens,
+                        const int32_t *prefix_lens, cp_segment *segs,
+                        int32_t seg_cap, int32_t *num_segs, int32_t *positions,
+                        int32_t *global_idx, int32_t tok_cap,
+                        int32_t *num_local, int32_t *padded_local);
+
+/*
+ * cp_restore_index -- host only, integer.
+ * The all-gathered buffer holds rank 0's N_0 local rows padded to
+ * padded_local slots, then rank 1's, and so on (C * padded_local slots).
+ * restore[g] is the slot of flattened new token g, so gathering the buffer
+ * by `restore` yields causal (flattened batch) order.  Padding slots are
+ * never referenced.
+ * In:  strategy, cp_size, num_reqs, new_lens (host).
+ * Out: restore[cap] (optional), *padded_local (optional).
+ * Errors: as cp_shard_plan; CP_ERR_SMALL_BUFFER if cap < sum(new_lens).
+ */
+cp_status cp_restore_index(int32_t strategy, int32_t cp_size, int32_t num_reqs,
+                           const int32_t *new_lens, int32_t *restore,
+                           int32_t cap, int32_t *padded_local);
+
+/*
+ * Arguments of cp_attn_fwd.
+ *
+ * Tensors are row-major with the head dim contiguous:
+ *   q  [num_q_rows][hq][dqk]    element (r,h,d) at q[r*q_row_stride + h*q_head_stride + d]
+ *   k  [num_kv_rows][hkv][dqk]
+ *   v  [num_kv_rows][hkv][dv]   may alias k (MLA latent: V = first dv columns of K)
+ *   o  [num_q_rows][hq][dv]     dtype o_dtype
+ *   lse [num_q_rows][hq]        fp32, natural log, element (r,h) at lse[r*lse_row_stride + h]
+ * Strides are in elements.  q, k, v and o must be 16-byte aligned and their
+ * strides multiples of 8 elements (bf16) / 4 elements (fp32).
+ *
+ * For row i of a segment, query head h (KV head h / (hq/hkv)), the visible
+ * keys are the KV rows j in [kv_begin, kv_end) with key position
+ * kpos(j) <= pos_begin + (i - q_begin) * pos_stride when causal != 0 (all of
+ * them when causal == 0).  kpos(j) = kv_pos[j] when kv_pos is non-NULL,
+ * else j - kv_begin.  With s_j = scale * <q, k_j>:
+ *   lse = ln sum_j exp(s_j),   o = sum_j exp(s_j - lse) v_j.
+ * A row with no visible key gets o = 0 and lse = -inf.
+ * Rows not covered by any segment are not written.
+ *
+ * Preconditions the library cannot check (violations give unspecified
+ * values, never an out-of-bounds access): each row is in at most one
+ * segment; kv_pos is strictly increasing over every segment's kv range.
+ *
+ * segs is a HOST array (the planner's output); kv_pos is a DEVICE array
+ * (int32, num_kv_rows entries) or NULL.  workspace is device memory of at
+ * least cp_attn_workspace_size bytes (NULL if that size is 0).
+ *
+ * Supported: dtype CP_BF16 with (dqk, dv) in {(64,64), (128,128), (192,128),
+ * (576,512)} and dtype CP_F32 with dqk, dv <= 128 (multiples of 4);
+ * o_dtype CP_BF16 or CP_F32; hq % hkv == 0.
+ */
+typedef struct {
+  int32_t dtype;        /* cp_dtype of q, k, v */
+  int32_t o_dtype;      /* cp_dtype of o */
+  int32_t num_q_rows;
+  int32_t num_kv_rows;
+  int32_t hq, hkv, dqk, dv;
+  float scale;
+  int32_t causal;
+  const void *q; int64_t q_row_stride, q_head_stride;
+  const void *k; int64_t k_row_stride, k_head_stride;
+  const void *v; int64_t v_row_stride, v_head_stride;
+  void *o;       int64_t o_row_stride, o_head_stride;
+  float *lse;    int64_t lse_row_stride;
+  const cp_segment *segs;  /* host */
+  int32_t num_segs;
+  const int32_t *kv_pos;   /* device, optional */
+  void *workspace;         /* device, optional */
+  size_t workspace_bytes;
+} cp_attn_args;
+
+/*
+ * cp_attn_workspace_size -- bytes of device workspace cp_attn_fwd needs for
+ * these arguments (0 for most shapes; the many-heads decode path keeps its
+ * split-KV partials there).  Only the shape fields and segs are read.
+ * Errors: as cp_attn_fwd's argument checks.
+ */
+cp_status cp_attn_workspace_size(const cp_attn_args *args, size_t *bytes);
+
+/*
+ * cp_attn_fwd -- enqueue the attention described by `args` on `stream`.
+ * Errors: CP_ERR_ARG (NULL pointers, hq % hkv != 0, a segment outside
+ * [0, num_q_rows) or [0, num_kv_rows), negative sizes, pos_stride < 0,
+ * misaligned pointers/strides), CP_ERR_UNSUPPORTED (dtype or head dims
+ * without a kernel), CP_ERR_SMALL_BUFFER (workspace too small),
+ * CP_ERR_DEVICE (launch failed).
+ */
+cp_status cp_attn_fwd(const cp_attn_args *args, void *stream);
+
+/*
+ * cp_lse_merge -- merge num_parts partial results of the same rows
+ * ("What is Context Parallelism", section 3.6, read as the generalised
+ * online softmax): per (row, head), with m = max_j L_j,
+ *   L = m + ln sum_j exp(L_j - m),   O = sum_j exp(L_j - L) O_j.
+ * Partials with L_j = -inf contribute nothing and their O_j is not read; if
+ * every partial is empty, O = 0 and L = -inf.
+ *
+ * o_parts: device, num_parts blocks of [rows][heads][dv] (contiguous, dtype
+ *   part_dtype), block j starting at element j * o_part_stride.
+ * lse_parts: device fp32, num_parts blocks of [rows][heads], block j at
+ *   element j * lse_part_stride.
+ * o_out: device [rows][heads][dv] of out_dtype; lse_out: device fp32
+ *   [rows][heads] or NULL.  Outputs must not overlap the inputs.
+ * Errors: CP_ERR_ARG (num_parts < 1, negative sizes, NULL pointers, strides
+ *   smaller than a block, misaligned pointers or dv not a multiple of 8),
+ *   CP_ERR_UNSUPPORTED (a dtype other than CP_F32/CP_BF16), CP_ERR_DEVICE.
+ */
+cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads,
+                       int32_t dv, const void *o_parts, int32_t part_dtype,
+                       int64_t o_part_stride, const float *lse_parts,
+                       int64_t lse_part_stride, void *o_out, int32_t out_dtype,
+                       float *lse_out, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *cp_status_str(int32_t status);
+
+/* Name and description of the HIP error behind the calling thread's most
+ * recent CP_ERR_DEVICE ("" if none yet).  Thread-local static storage, valid
+ * until the thread's next failing call. */
+const char *cp_last_error(void);
+
+/* Library version, "major.minor.patch" (static storage). */
+const char *cp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

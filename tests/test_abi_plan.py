@@ -1,0 +1,233 @@
+"""CPU tests of the C ABI: exported symbols, the planner and restore index
+bit-exact against the index oracle, and every host-side error path."""
+import ctypes
+import random
+import re
+
+import numpy as np
+import pytest
+
+import context_causal_attention_cp_amd as cp
+from context_causal_attention_cp_amd import _lib
+from oracle import index_oracle as ix
+import workloads
+
+
+def _header_functions():
+    import os
+    from conftest import ROOT
+    src = open(os.path.join(ROOT, "include", "cp_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    names = _header_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert cp.version().count(".") == 2
+    assert cp.status_str(0) == "CP_OK"
+
+
+def _cmp_plan(strategy, C, lens, pre):
+    for r in range(C):
+        got = cp.shard_plan(strategy, C, r, lens, pre)
+        toks = ix.rank_tokens(strategy, C, r, lens, pre)
+        segs = ix.segments(strategy, C, r, lens, pre)
+        assert got.num_local == len(toks)
+        assert got.padded_local == ix.padded_local(strategy, C, lens, pre)
+        assert got.positions.tolist() == [t.pos for t in toks]
+        assert got.global_idx.tolist() == [t.g for t in toks]
+        assert [s.astuple() for s in got.segments] == \
+            [(s.req, s.q_begin, s.q_end, s.pos_begin, s.pos_stride, s.kv_begin, s.kv_end)
+             for s in segs]
+    restore, pad = cp.restore_index(strategy, C, lens)
+    want, wpad = ix.restore_index(strategy, C, lens)
+    assert restore.tolist() == want and pad == wpad
+
+
+@pytest.mark.parametrize("strategy", ["zigzag", "interleave"])
+def test_planner_matches_oracle_random(strategy):
+    rnd = random.Random(42 if strategy == "zigzag" else 43)
+    for _ in range(250):
+        C = rnd.randint(1, 8)
+        B = rnd.randint(0, 5)
+        lens = [rnd.randint(0, 70) for _ in range(B)]
+        pre = [rnd.randint(0, 50) if rnd.random() < 0.5 else 0 for _ in range(B)]
+        _cmp_plan(strategy, C, lens, pre)
+
+
+@pytest.mark.parametrize("name", ["zigzag_t256", "zigzag_t8192_p1024", "interleave_b12"])
+def test_planner_matches_oracle_workloads(name):
+    w = workloads.get(name)
+    _cmp_plan(w.strategy, w.cp_size, list(w.new_lens), list(w.prefix_lens))
+
+
+def test_planner_mla_131072_all_ranks():
+    # the long-context zigzag workload: every rank owns 2 blocks of 8192
+    for r in range(8):
+        p = cp.shard_plan("zigzag", 8, r, [131072], [0])
+        assert [s.astuple() for s in p.segments] == [
+            (0, 0, 8192, 8192 * r, 1, 0, 8192 * (r + 1)),
+            (0, 8192, 16384, 8192 * (15 - r), 1, 0, 8192 * (16 - r))]
+        assert p.num_local == p.padded_local == 16384
+
+
+def test_planner_null_prefix_and_empty_batch():
+    a = cp.shard_plan("interleave", 3, 1, [4, 5])
+    b = cp.shard_plan("interleave", 3, 1, [4, 5], [0, 0])
+    assert [s.astuple() for s in a.segments] == [s.astuple() for s in b.segments]
+    e = cp.shard_plan("zigzag", 4, 2, [])
+    assert e.num_local == 0 and e.segments == [] and e.padded_local == 0
+
+
+def _raw_plan(strategy, C, r, lens, pre, seg_cap, tok_cap, want_arrays=True):
+    L = _lib._lib
+    tl = np.asarray(lens, dtype=np.int32)
+    pl = np.asarray(pre, dtype=np.int32)
+    P32 = ctypes.POINTER(ctypes.c_int32)
+    segs = (_lib.Segment * max(1, seg_cap))()
+    pos = np.zeros(max(1, tok_cap), dtype=np.int32)
+    nseg, nloc, pad = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = L.cp_shard_plan(strategy, C, r, len(lens), tl.ctypes.data_as(P32), pl.ctypes.data_as(P32),
+                         segs if want_arrays else None, seg_cap, ctypes.byref(nseg),
+                         pos.ctypes.data_as(P32) if want_arrays else None, None, tok_cap,
+                         ctypes.byref(nloc), ctypes.byref(pad))
+    return st, nseg.value, nloc.value, pad.value
+
+
+def test_plan_error_paths():
+    ok = _raw_plan(0, 4, 1, [16], [0], 8, 64)
+    assert ok == (_lib.CP_OK, 2, 4, 4)
+    assert _raw_plan(2, 4, 1, [16], [0], 8, 64)[0] == _lib.CP_ERR_ARG      # strategy
+    assert _raw_plan(0, 0, 0, [16], [0], 8, 64)[0] == _lib.CP_ERR_ARG      # C = 0
+    assert _raw_plan(0, 4, 4, [16], [0], 8, 64)[0] == _lib.CP_ERR_ARG      # rank = C
+    assert _raw_plan(0, 4, -1, [16], [0], 8, 64)[0] == _lib.CP_ERR_ARG
+    assert _raw_plan(0, 4, 0, [-3], [0], 8, 64)[0] == _lib.CP_ERR_ARG      # negative length
+    assert _raw_plan(1, 4, 0, [3], [-1], 8, 64)[0] == _lib.CP_ERR_ARG      # negative prefix
+    assert _raw_plan(0, 2, 0, [2**30, 2**30], [0, 0], 8, 64)[0] == _lib.CP_ERR_ARG  # overflow
+    # too small: sizes are still reported
+    st, nseg, nloc, pad = _raw_plan(0, 4, 1, [16], [0], 1, 64)
+    assert (st, nseg, nloc, pad) == (_lib.CP_ERR_SMALL_BUFFER, 2, 4, 4)
+    st, nseg, nloc, pad = _raw_plan(0, 4, 1, [16], [0], 8, 3)
+    assert (st, nseg, nloc, pad) == (_lib.CP_ERR_SMALL_BUFFER, 2, 4, 4)
+    # size query with NULL arrays
+    assert _raw_plan(0, 4, 1, [16], [0], 0, 0, want_arrays=False) == (_lib.CP_OK, 2, 4, 4)
+
+
+def test_restore_error_paths():
+    L = _lib._lib
+    P32 = ctypes.POINTER(ctypes.c_int32)
+    tl = np.asarray([5, 3], dtype=np.int32)
+    out = np.zeros(8, dtype=np.int32)
+    pad = ctypes.c_int32(-1)
+    assert L.cp_restore_index(1, 4, 2, tl.ctypes.data_as(P32), out.ctypes.data_as(P32), 7,
+                              ctypes.byref(pad)) == _lib.CP_ERR_SMALL_BUFFER
+    assert pad.value == 2
+    assert L.cp_restore_index(1, 4, 2, tl.ctypes.data_as(P32), None, 0,
+                              ctypes.byref(pad)) == _lib.CP_OK
+    assert L.cp_restore_index(1, 0, 2, tl.ctypes.data_as(P32), out.ctypes.data_as(P32), 8,
+                              ctypes.byref(pad)) == _lib.CP_ERR_ARG
+    assert L.cp_restore_index(1, 4, 2, tl.ctypes.data_as(P32), out.ctypes.data_as(P32), 8,
+                              ctypes.byref(pad)) == _lib.CP_OK
+    assert out.tolist() == ix.restore_index("interleave", 4, [5, 3])[0]
+
+
+# ---------------------------------------------------------------- attn / merge argument checks
+# Every case below must fail validation before anything touches a device, so
+# the fake, never-dereferenced device addresses are safe on a CPU-only host.
+
+FAKE = 0x10000
+
+
+def _args(**kw):
+    a = _lib.AttnArgs()
+    segs = (_lib.Segment * 2)(_lib.Segment(0, 0, 4, 0, 1, 0, 4), _lib.Segment(0, 4, 8, 12, 1, 0, 16))
+    base = dict(dtype=_lib.CP_BF16, o_dtype=_lib.CP_BF16, num_q_rows=8, num_kv_rows=16, hq=4,
+                hkv=2, dqk=128, dv=128, scale=0.1, causal=1,
+                q=FAKE, q_row_stride=512, q_head_stride=128,
+                k=FAKE, k_row_stride=256, k_head_stride=128,
+                v=FAKE, v_row_stride=256, v_head_stride=128,
+                o=FAKE, o_row_stride=512, o_head_stride=128,
+                lse=FAKE, lse_row_stride=4, num_segs=2)
+    base.update(kw)
+    for k_, v_ in base.items():
+        setattr(a, k_, v_)
+    a.segs = kw.get("segs", segs)
+    return a, segs
+
+
+def _fwd(**kw):
+    a, keep = _args(**kw)
+    st = _lib._lib.cp_attn_fwd(ctypes.byref(a), None)
+    del keep
+    return st
+
+
+def _ws(**kw):
+    a, keep = _args(**kw)
+    n = ctypes.c_size_t(123)
+    st = _lib._lib.cp_attn_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    del keep
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(hq=3), _lib.CP_ERR_ARG),                     # hq % hkv
+    (dict(hkv=0), _lib.CP_ERR_ARG),
+    (dict(dqk=96), _lib.CP_ERR_UNSUPPORTED),
+    (dict(dv=64), _lib.CP_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.CP_ERR_UNSUPPORTED),
+    (dict(o_dtype=9), _lib.CP_ERR_UNSUPPORTED),
+    (dict(dtype=_lib.CP_F32, dqk=192, dv=128), _lib.CP_ERR_UNSUPPORTED),
+    (dict(num_q_rows=7), _lib.CP_ERR_ARG),             # segment beyond the q rows
+    (dict(num_kv_rows=15), _lib.CP_ERR_ARG),           # segment beyond the kv rows
+    (dict(num_q_rows=-1), _lib.CP_ERR_ARG),
+    (dict(scale=float("nan")), _lib.CP_ERR_ARG),
+    (dict(q=0), _lib.CP_ERR_ARG),                      # NULL
+    (dict(lse=0), _lib.CP_ERR_ARG),
+    (dict(q=FAKE + 8), _lib.CP_ERR_ARG),               # misaligned
+    (dict(k_row_stride=250), _lib.CP_ERR_ARG),         # stride not a multiple of 8
+    (dict(o_head_stride=130), _lib.CP_ERR_ARG),
+])
+def test_attn_arg_errors(kw, want):
+    assert _fwd(**kw) == want
+
+
+def test_attn_segment_errors():
+    bad = [
+        _lib.Segment(0, 5, 4, 0, 1, 0, 4),       # q_end < q_begin
+        _lib.Segment(0, -1, 4, 0, 1, 0, 4),
+        _lib.Segment(0, 0, 4, 0, -1, 0, 4),      # negative stride
+        _lib.Segment(0, 0, 4, 0, 1, 3, 2),       # kv_end < kv_begin
+        _lib.Segment(0, 0, 4, 2**30, 1, 0, 4),   # positions out of range
+    ]
+    for s in bad:
+        arr = (_lib.Segment * 1)(s)
+        assert _fwd(segs=arr, num_segs=1) == _lib.CP_ERR_ARG, s
+    assert _fwd(segs=None, num_segs=1) == _lib.CP_ERR_ARG
+
+
+def test_workspace_size_query():
+    assert _ws() == (_lib.CP_OK, 0)
+    assert _ws(hq=3)[0] == _lib.CP_ERR_ARG
+
+
+def test_merge_arg_errors():
+    L = _lib._lib
+    def m(parts=2, rows=4, heads=2, dv=128, op=FAKE, pdt=1, ops=1024, lp=FAKE, lps=8,
+          oo=FAKE, odt=1, lo=FAKE):
+        return L.cp_lse_merge(parts, rows, heads, dv, op, pdt, ops, lp, lps, oo, odt, lo, None)
+    assert m(parts=0) == _lib.CP_ERR_ARG
+    assert m(rows=-1) == _lib.CP_ERR_ARG
+    assert m(dv=12) == _lib.CP_ERR_ARG
+    assert m(dv=192) == _lib.CP_ERR_ARG          # 24 lanes do not tile a workgroup
+    assert m(pdt=5) == _lib.CP_ERR_UNSUPPORTED
+    assert m(odt=5) == _lib.CP_ERR_UNSUPPORTED
+    assert m(op=0) == _lib.CP_ERR_ARG
+    assert m(op=FAKE + 4) == _lib.CP_ERR_ARG
+    assert m(ops=1000) == _lib.CP_ERR_ARG        # parts overlap
+    assert m(lps=7) == _lib.CP_ERR_ARG
+    assert m(rows=0) == _lib.CP_OK               # nothing to do, nothing enqueued

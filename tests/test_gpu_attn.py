@@ -1,0 +1,137 @@
+"""GPU parity of cp_attn_fwd against the oracle on small shapes: several
+tiles with ragged tails, every kernel variant, zigzag and interleave with
+cached prefixes, GQA, explicit key positions (ring partials), empty rows,
+non-causal, fp32 output."""
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_cp_amd as cp
+from oracle import attn_oracle as ao
+from oracle import index_oracle as ix
+from gpu_helpers import compare, f64, oracle_segments, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _tensors(n_new, n_kv, hq, hkv, dqk, dv, dtype, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn((n_new, hq, dqk), generator=g, device=DEV).to(td)
+    k = torch.randn((n_kv, hkv, dqk), generator=g, device=DEV).to(td)
+    v = torch.randn((n_kv, hkv, dv), generator=g, device=DEV).to(td)
+    return q, k, v
+
+
+CASES = [
+    # strategy, C, lens, prefixes, hq, hkv, dqk, dv, dtype
+    ("zigzag", 2, [300, 77], [50, 0], 8, 2, 128, 128, "bf16"),
+    ("zigzag", 3, [517], [33], 4, 4, 192, 128, "bf16"),
+    ("interleave", 4, [5, 3, 200, 130], [0, 7, 100, 0], 4, 1, 64, 64, "bf16"),
+    ("interleave", 3, [129, 1, 260], [300, 0, 5], 8, 8, 192, 128, "bf16"),
+    ("zigzag", 4, [256], [0], 4, 4, 64, 64, "f32"),
+    ("interleave", 2, [70, 131], [3, 40], 4, 2, 128, 128, "f32"),
+    ("zigzag", 1, [190], [0], 2, 1, 128, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-C{c[1]}-{c[6]}x{c[7]}-{c[8]}" for c in CASES])
+def test_shard_attention_small(case):
+    strategy, C, lens, pre, hq, hkv, dqk, dv, dtype = case
+    n_new, n_kv = sum(lens), sum(p + t for p, t in zip(pre, lens))
+    q, k, v = _tensors(n_new, n_kv, hq, hkv, dqk, dv, dtype, seed=sum(lens) + C)
+    k64, v64, q64 = f64(k), f64(v), f64(q)
+    scale = 1.0 / np.sqrt(dqk)
+    for r in range(C):
+        say(f"attn {strategy} C={C} r={r} lens={lens} pre={pre} heads={hq}/{hkv} d={dqk}/{dv} {dtype}")
+        plan = cp.shard_plan(strategy, C, r, lens, pre)
+        if plan.num_local == 0:
+            continue
+        gidx = torch.from_numpy(plan.global_idx.astype(np.int64)).to(DEV)
+        o, lse = cp.attn_fwd(q.index_select(0, gidx), k, v, plan, scale)
+        torch.cuda.synchronize()
+        toks = ix.rank_tokens(strategy, C, r, lens, pre)
+        segs = oracle_segments(strategy, C, r, lens, pre)
+        ro, rl = ao.shard_attention(q64[[t.g for t in toks]], k64, v64, segs, hq, hkv, scale)
+        compare(f64(o), f64(lse), ro, rl, range(plan.num_local), dtype, f"rank {r}")
+
+
+@pytest.mark.parametrize("dqk,dv", [(192, 128), (128, 128), (64, 64)])
+def test_ring_partials_with_key_positions(dqk, dv):
+    """Rank r's queries against rank j's zigzag KV pair, masked by explicit
+    key positions; partials vs oracle, merged vs dense."""
+    C, T, H = 4, 640, 2
+    q, k, v = _tensors(T, T, H, H, dqk, dv, "bf16", seed=dqk + dv)
+    q64, k64, v64 = f64(q), f64(k), f64(v)
+    scale = 1.0 / np.sqrt(dqk)
+    for r in (0, 3):
+        plan = cp.shard_plan("zigzag", C, r, [T], [0])
+        mine = plan.global_idx.astype(np.int64)
+        q_loc = q.index_select(0, torch.from_numpy(mine).to(DEV))
+        o_parts, l_parts = [], []
+        for j in range(C):
+            say(f"ring d={dqk}/{dv} rank {r} kv pair {j}")
+            rows_j = cp.shard_plan("zigzag", C, j, [T], [0]).global_idx.astype(np.int64)
+            idx = torch.from_numpy(rows_j).to(DEV)
+            kj, vj = k.index_select(0, idx), v.index_select(0, idx)
+            kv_pos = idx.to(torch.int32)
+            segs = [cp.Segment(s.req, s.q_begin, s.q_end, s.pos_begin, s.pos_stride, 0, len(rows_j))
+                    for s in plan.segments]
+            o, l = cp.attn_fwd(q_loc, kj, vj, segs, scale, kv_pos=kv_pos)
+            torch.cuda.synchronize()
+            osegs = [ix.Segment(s.req, s.q_begin, s.q_end, s.pos_begin, s.pos_stride, 0,
+                                len(rows_j)) for s in oracle_segments("zigzag", C, r, [T], [0])]
+            ro, rl = ao.shard_attention(q64[mine], k64[rows_j], v64[rows_j], osegs, H, H, scale,
+                                        kv_pos=rows_j)
+            compare(f64(o), f64(l), ro, rl, range(len(mine)), "bf16", f"partial {j}")
+            o_parts.append(o)
+            l_parts.append(l)
+        mo, ml = cp.lse_merge(torch.stack(o_parts), torch.stack(l_parts))
+        torch.cuda.synchronize()
+        dense_o, dense_l = ao.shard_attention(q64[mine], k64, v64,
+                                              oracle_segments("zigzag", C, r, [T], [0]), H, H, scale)
+        compare(f64(mo), f64(ml), dense_o, dense_l, range(len(mine)), "bf16", "merged")
+
+
+def test_empty_kv_segment_and_noncausal_and_f32_out():
+    hq = hkv = 2
+    q, k, v = _tensors(40, 64, hq, hkv, 128, 128, "bf16", seed=5)
+    q64, k64, v64 = f64(q), f64(k), f64(v)
+    segs = [cp.Segment(0, 0, 10, 0, 1, 0, 0),       # sees no KV row at all
+            cp.Segment(1, 10, 40, 3, 2, 5, 64)]     # stride-2 positions
+    say("empty-kv segment + causal, bf16 out")
+    o, l = cp.attn_fwd(q, k, v, segs, 0.1)
+    torch.cuda.synchronize()
+    osegs = [ix.Segment(*s.astuple()) for s in segs]
+    ro, rl = ao.shard_attention(q64, k64, v64, osegs, hq, hkv, 0.1)
+    compare(f64(o), f64(l), ro, rl, range(40), "bf16", "causal")
+    say("non-causal, fp32 out")
+    o, l = cp.attn_fwd(q, k, v, segs, 0.1, causal=False, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = ao.shard_attention(q64, k64, v64, osegs, hq, hkv, 0.1, causal=False)
+    compare(f64(o), f64(l), ro, rl, range(40), "bf16", "non-causal")
+
+
+def test_zero_query_closed_form_small():
+    """q = 0: every visible score is 0, so LSE = ln(#visible keys)."""
+    lens, pre, C = [1000, 37], [200, 5], 2
+    for dqk, dv in [(128, 128), (192, 128), (64, 64)]:
+        _, k, v = _tensors(1, sum(p + t for p, t in zip(pre, lens)), 4, 2, dqk, dv, "bf16", 3)
+        for r in range(C):
+            plan = cp.shard_plan("zigzag", C, r, lens, pre)
+            q = torch.zeros((plan.num_local, 4, dqk), device=DEV, dtype=torch.bfloat16)
+            o, l = cp.attn_fwd(q, k, v, plan, 0.3)
+            torch.cuda.synchronize()
+            want = np.log(plan.positions.astype(np.float64) + 1.0)
+            assert np.max(np.abs(f64(l) - want[:, None])) < 1e-3
+
+
+def test_repeatable_bitwise():
+    q, k, v = _tensors(300, 300, 4, 4, 192, 128, "bf16", seed=11)
+    plan = cp.shard_plan("zigzag", 1, 0, [300], [0])
+    a = cp.attn_fwd(q, k, v, plan, 0.07)
+    b = cp.attn_fwd(q, k, v, plan, 0.07)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
