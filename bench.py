@@ -35,8 +35,44 @@ def _args():
     ap.add_argument("--rank", type=int, default=0, help="CP rank whose share is timed")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
+
+
+def _copy_calibration(steps):
+    """A copy of known size: 1 GiB read + 1 GiB written per launch.  Its
+    FETCH_SIZE / WRITE_SIZE counters give the factor between counter KiB
+    and bytes moved."""
+    import torch
+    src = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4,
+                      "copy_calibration_bytes_written": dst.numel() * 4,
+                      "launches": steps}), flush=True)
+
+
+def _profiled_traffic(kernel: str, source: str):
+    """HBM bytes per launch (read + write) that rocprofv3 counters measured
+    for ``kernel``, from the summaries under profiles/; None when no summary
+    was taken with the kernel's current source."""
+    import hashlib
+    src = os.path.join(ROOT, "context_causal_attention_cp_amd", "csrc", source)
+    with open(src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()[:16]
+    pdir = os.path.join(ROOT, "profiles")
+    for fn in sorted(os.listdir(pdir)) if os.path.isdir(pdir) else []:
+        with open(os.path.join(pdir, fn)) as f:
+            for line in f:
+                if not line.startswith("TRAFFIC "):
+                    continue
+                kv = dict(x.split("=", 1) for x in line.split()[1:])
+                if kv.get("kernel") == kernel and kv.get("sha256_16") == h:
+                    return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def _useful_flops(pairs_per_head, hq, dqk, dv):
@@ -54,6 +90,9 @@ def main():
               f"that GPU, so --gpus {a.gpus} is not a configuration this build measures.",
               file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        _copy_calibration(a.steps)
+        return
     import numpy as np
     import torch
 
@@ -117,6 +156,11 @@ def main():
     attn_launch_ms = attn_ms_avg / C
     achieved_tflops = flops / (attn_ms_avg * 1e-3) / 1e12
 
+    # attention algorithmic bytes per launch: Q, K_j, V_j, kv_pos read once,
+    # O and LSE written once
+    kj0 = kv[0][0]
+    attn_bytes = (q_loc.numel() * 2 + kj0.numel() * 2 + kv[0][1].numel() * 2 + kv[0][2].numel() * 4
+                  + n * w.hq * (w.dv * 2 + 4))
     # merge algorithmic bytes: live partial rows' O (bf16) + every LSE + outputs
     lp = l_parts.isfinite()
     live_rows = int(lp.sum().item())                   # (row, head, part) triples
@@ -149,7 +193,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": _profiled_traffic("attn_fwd_bf16_kernel<192,128>", "attn_fwd_bf16.hip"),
+            "algorithmic_bytes": attn_bytes,
             "avg_launch_ms": round(attn_launch_ms, 4),
         },
         "merge": {
@@ -158,6 +203,7 @@ def main():
             "algorithmic_bytes": merge_bytes,
             "GB/s": round(merge_gbs, 1),
             "frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4),
+            "traffic": _profiled_traffic("lse_merge_kernel<bf16,bf16>", "lse_merge.hip"),
         },
     }
     del kv
