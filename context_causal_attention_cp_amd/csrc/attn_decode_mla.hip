@@ -1,0 +1,372 @@
+// Decode-CP shard attention for the MLA-absorbed shape on gfx950.
+//
+// "What is Context Parallelism" (blog): section 2.2 -- decode is a
+// memory-bound scan of a large KV cache; the cache is sharded along the
+// sequence (token i on shard i mod W) and the small Q is brought to every
+// shard (section 3.3); each shard returns its normalised partial output and
+// log-sum-exp for an LSE merge (section 3.6).  Section 4.2 -- with the
+// absorbed MLA form every query head attends directly to the shared latent
+// row: K = [c_KV (512) | k_pe (64)], and V is the first 512 columns of the
+// same row.
+//
+// One workgroup (8 waves) computes, for one query row and 128 query heads of
+// one KV head, the partial attention over one contiguous slice of the
+// shard's keys:
+//   * the heads are the MFMA N dimension, 16 per wave (v_mfma_f32_16x16x32_bf16);
+//     each wave keeps its 16 x 576 Q fragment in VGPRs and its 512 x 16 fp32
+//     O^T accumulator in AGPRs (two waves per SIMD);
+//   * key tiles of 32 latent rows (36 KiB) are copied HBM -> LDS with
+//     global_load_lds (no register staging), three tiles in flight;
+//   * S^T = K Q^T reads K rows from LDS; O^T += V^T P^T reads V^T from the
+//     same row-major tile with the transposing read ds_read_b64_tr_b16, so
+//     each latent row crosses HBM once and sits in LDS once;
+//   * the tile is XOR-swizzled in 16-byte chunks so that the row reads and
+//     the transposing reads are free of bank conflicts;
+//   * each lane keeps the softmax reference max of its head; the waves only
+//     exchange row maxima (and rescale the accumulator) when some lane's
+//     tile max exceeds the reference by more than 2^8;
+// and writes the slice's normalised partial (O_s, LSE_s) to the workspace.
+// A second kernel merges the slices of each (row, head) by LSE.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace cpattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int NW = 8;                    // waves
+constexpr int NT = 64 * NW;              // threads
+constexpr int HW = 16;                   // heads per wave
+constexpr int HT = kDecodeHeadsPerBlock; // heads per workgroup
+static_assert(HT == HW * NW, "heads per workgroup");
+constexpr int BN = 32;                   // keys per tile
+constexpr int DQK = 576, DV = 512;
+constexpr int KCH = DQK / 8;             // 16-byte chunks per latent row
+constexpr int TILE_CH = BN * KCH;        // 2304 chunks = 36 KiB
+constexpr int TILE_WI = TILE_CH / 64;    // 36 wave-instructions of LDS DMA per tile
+constexpr int NBUF = 3;
+constexpr int QS = DQK / 32;             // MFMA k-steps for S (18)
+constexpr int OB = DV / 16;              // 16-row dv blocks of O^T (32)
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescale = 8.0f;         // log2 headroom before the reference max moves
+static_assert(TILE_WI == 36, "DMA split below assumes 36 instructions per tile");
+
+// XOR swizzle of the 16-byte chunk index within a latent row; it stays in
+// its aligned group of 8 chunks (72 is a multiple of 8).  With key bits
+// k0..k3: f = (k0^k3) | (k0^k1)<<1 | (k0^k2)<<2.  Row reads (16 consecutive
+// keys, one chunk) and transposing reads (8 consecutive keys, 2 chunks) then
+// hit distinct bank groups under both 32- and 64-bank LDS organisations.
+__device__ inline int swz(int key) {
+  const int k0 = key & 1, k1 = (key >> 1) & 1, k2 = (key >> 2) & 1, k3 = (key >> 3) & 1;
+  return (k0 ^ k3) | ((k0 ^ k1) << 1) | ((k0 ^ k2) << 2);
+}
+
+__device__ inline uint32_t pack_bf16(float a, float b) {
+  const __bf16 lo = (__bf16)a, hi = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// max / sum over the four 16-lane groups that hold the same head
+__device__ inline float max_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ inline float sum_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+// vmcnt wait with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ inline void decode_item(const DecodeLaunch &D, int item, int &si, int &row, int &kvh,
+                                   int &ht) {
+  si = 0;
+  for (int i = 1; i < D.num_segs; ++i)
+    if (item >= D.s[i].tile_begin) si = i;
+  int rem = item - D.s[si].tile_begin;
+  ht = rem % D.htiles;
+  rem /= D.htiles;
+  kvh = rem % D.hkv;
+  row = rem / D.hkv;
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
+  __shared__ __attribute__((aligned(1024))) u32x4 sk[NBUF][TILE_CH];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int item = blockIdx.x / D.nsplit, split = blockIdx.x % D.nsplit;
+  if (item >= D.items) return;
+  int si, row, kvh, ht;
+  decode_item(D, item, si, row, kvh, ht);
+  const SegDesc sd = D.s[si];
+  const int G = p.hq / p.hkv;
+  const int hl = ht * HT + w * HW + n;           // head within the KV group
+  const bool hvalid = hl < G;
+  const int h = kvh * G + hl;
+  const int64_t qrow = (int64_t)sd.q_begin + row;
+  const int qpos = sd.pos_begin + row * sd.pos_stride;
+
+  // this workgroup's key slice
+  const int chunk = ((sd.kv_len + D.nsplit - 1) / D.nsplit + BN - 1) / BN * BN;
+  const int k_lo = min(sd.kv_len, split * chunk);
+  const int k_hi = min(sd.kv_len, k_lo + chunk);
+  const int32_t *kvp = p.kv_pos ? p.kv_pos + sd.kv_begin : nullptr;
+  auto key_pos = [&](int j) -> int { return kvp ? kvp[j] : j; };
+  // keys past the query's position end the slice early (positions increase)
+  int k_vis = k_hi;
+  if (p.causal && k_hi > k_lo && key_pos(k_hi - 1) > qpos) {
+    int lo = k_lo, hi = k_hi;  // first key with position > qpos
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (key_pos(mid) <= qpos) lo = mid + 1; else hi = mid;
+    }
+    k_vis = lo;
+  }
+  const int ntiles = (k_vis - k_lo + BN - 1) / BN;
+
+  // Q fragments: B operand of S^T = K Q^T (n = head, k = d: 8 per lane group)
+  bf16x8 qf[QS];
+  {
+    const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)h * p.q_hs + 8 * g;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (hvalid) x = *(const u32x4 *)(qp + 32 * s);
+      qf[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // LDS DMA: waves 0-3 issue 5 and waves 4-7 issue 4 of the 36 instructions
+  const __bf16 *kbase = (const __bf16 *)p.k + (int64_t)sd.kv_begin * p.k_rs + (int64_t)kvh * p.k_hs;
+  const int wi0 = w < 4 ? 5 * w : 20 + 4 * (w - 4);
+  const int wn = w < 4 ? 5 : 4;
+  // LDS DMA goes through a buffer resource that ends at the slice end: rows
+  // past k_hi read as zeros (hardware range check), so the last tile needs no
+  // clamping.  Per-lane byte offsets are relative to the tile's first row.
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)kbase, (short)0, (int)((int64_t)k_hi * p.k_rs * 2), 0x00020000);
+  auto issue = [&](int t) {
+    const uint32_t row0 = (uint32_t)((k_lo + t * BN) * p.k_rs) * 2u;
+    u32x4 *dst = sk[t % NBUF];
+    // recomputed per tile (cheap integer math) instead of kept live in VGPRs
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      if (i < wn) {
+        const int slot = (wi0 + i) * 64 + ln;
+        const int key = slot / KCH, cs = slot % KCH;
+        const uint32_t off = (uint32_t)(key * p.k_rs + (cs ^ swz(key)) * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            krsrc, (__attribute__((address_space(3))) void *)(dst + (wi0 + i) * 64), 16,
+            row0 + off, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x4 oacc[OB];
+#pragma unroll
+  for (int b = 0; b < OB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oacc[b][i] = 0.f;
+  float m_ref = -INFINITY;  // reference max of this lane's head (log2 units)
+  float l_run = 0.f;        // this lane's partial row sum
+  const float sl2 = p.scale_log2;
+
+  // Per-lane LDS byte offsets.  The swizzle only touches the low 3 bits of
+  // the chunk index, so every read below is one of a few per-lane bases plus
+  // a compile-time offset (128 bytes per group of 8 chunks).
+  //  row reads (QK): key 16*mb + n, chunk 4*st + g = 8*(st>>1) + (4*(st&1) + g).
+  //  The swizzle only depends on key bits 0..3, so key + 16 is the same read
+  //  shifted by 16 rows (kRow16 bytes).
+  constexpr int kRow16 = 16 * KCH * 16;
+  int qk_base[2];
+#pragma unroll
+  for (int odd = 0; odd < 2; ++odd) qk_base[odd] = 16 * (n * KCH + ((4 * odd + g) ^ swz(n)));
+  //  transposing reads (PV): lane li of group g addresses key 4g + li/4 (+16),
+  //  dv 16*b + 4*(li%4): chunk 2*b + (li%4)/2 = 8*(b>>2) + (2*(b&3) + (li%4)/2),
+  //  byte 8*(li&1) inside the chunk
+  int tr_base[4];
+  {
+    const int key = 4 * g + (n >> 2);
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4)
+      tr_base[b4] = 16 * (key * KCH + ((2 * b4 + ((n & 3) >> 1)) ^ swz(key))) + 8 * (n & 1);
+  }
+
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) {
+      if (w < 4) wait_vm<5>(); else wait_vm<4>();
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (t + 2 < ntiles) issue(t + 2);
+    const char *tile = (const char *)sk[t % NBUF];
+    const int j0 = k_lo + t * BN;
+
+    // ---- S^T = K Q^T : two 16-key blocks x 16 heads
+    f32x4 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[mb][i] = 0.f;
+#pragma unroll
+      for (int st = 0; st < QS; ++st) {
+        const bf16x8 a =
+            *(const bf16x8 *)(tile + qk_base[st & 1] + kRow16 * mb + 128 * (st >> 1));
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], s[mb], 0, 0, 0);
+      }
+    }
+    // ---- mask (keys at or past k_vis are after the query or past the
+    // slice; positions increase), lane-local max
+    const bool full = j0 + BN <= k_vis;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float u = s[mb][i] * sl2;
+        if (!full) u = (j0 + 16 * mb + 4 * g + i < k_vis) ? u : -INFINITY;
+        s[mb][i] = u;
+        mx = fmaxf(mx, u);
+      }
+    // move the reference (wave-wide, rare) only if some lane outgrew it by > 2^8
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescale) != 0) {
+      const float m_new = fmaxf(m_ref, max_groups(mx));
+      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < OB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[b][i] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    // P as the B operand: element e <-> key (e<4 ? 4g+e : 16+4g+e-4)
+    u32x4 pk;
+    float ls = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float p0 = exp2f(s[mb][0] - m_use), p1 = exp2f(s[mb][1] - m_use);
+      const float p2 = exp2f(s[mb][2] - m_use), p3 = exp2f(s[mb][3] - m_use);
+      ls += (p0 + p1) + (p2 + p3);
+      pk[2 * mb] = pack_bf16(p0, p1);
+      pk[2 * mb + 1] = pack_bf16(p2, p3);
+    }
+    l_run += ls;
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+    // ---- O^T += V^T P^T : V^T from the same tile by transposing reads
+#pragma unroll
+    for (int b = 0; b < OB; ++b) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(tile + tr_base[b & 3] + 128 * (b >> 2)));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(tile + tr_base[b & 3] + kRow16 + 128 * (b >> 2)));
+      // whole-vector bit casts: building the operand element by element from
+      // the 16-bit lanes of the transposing reads miscompiles (every element
+      // becomes element 0)
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+      oacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[b], 0, 0, 0);
+    }
+  }
+
+  // ---- normalised partial of this slice -> workspace
+  const float l_tot = sum_groups(l_run);
+  if (!hvalid) return;
+  const bool any = l_tot > 0.f;
+  const float inv = any ? 1.f / l_tot : 0.f;
+  const int64_t part = (int64_t)item * D.nsplit + split;
+  const int hb = w * HW + n;
+  float *wo = D.ws_o + (part * HT + hb) * DV + 4 * g;
+  if (g == 0) D.ws_lse[part * HT + hb] = any ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int b = 0; b < OB; ++b)
+    *(float4 *)(wo + 16 * b) =
+        make_float4(oacc[b][0] * inv, oacc[b][1] * inv, oacc[b][2] * inv, oacc[b][3] * inv);
+}
+
+// Merge of the slices of one (row, head): one wave per (item, head), 8 dv
+// elements per lane, LSE merge over the slices.
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(const AttnParams p,
+                                                                  const DecodeLaunch D) {
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int item = wv / HT, hloc = wv % HT;
+  if (item >= D.items) return;
+  int si, row, kvh, ht;
+  decode_item(D, item, si, row, kvh, ht);
+  const SegDesc sd = D.s[si];
+  const int G = p.hq / p.hkv;
+  const int hl = ht * HT + hloc;
+  if (hl >= G) return;
+  const int h = kvh * G + hl;
+  const int64_t qrow = (int64_t)sd.q_begin + row;
+  const int64_t part0 = (int64_t)item * D.nsplit;
+  float m = -INFINITY;
+  for (int s = 0; s < D.nsplit; ++s) m = fmaxf(m, D.ws_lse[(part0 + s) * HT + hloc]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < D.nsplit; ++s) {
+      const float ls = D.ws_lse[(part0 + s) * HT + hloc];
+      if (ls == -INFINITY) continue;
+      const float wgt = expf(ls - m);
+      wsum += wgt;
+      const float *src = D.ws_o + ((part0 + s) * HT + hloc) * DV + lane * 8;
+      const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
+      acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
+      acc[4] += wgt * b.x; acc[5] += wgt * b.y; acc[6] += wgt * b.z; acc[7] += wgt * b.w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (p.o_bf16) {
+    __bf16 *op = (__bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + lane * 8;
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+    *(u32x4 *)op = v;
+  } else {
+    float *op = (float *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + lane * 8;
+    *(float4 *)op = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    *(float4 *)(op + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  }
+  if (lane == 0) p.lse[qrow * p.lse_rs + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode_mla(const AttnParams &p, const DecodeLaunch &D, hipStream_t stream) {
+  if (D.items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_decode_mla_kernel, dim3((unsigned)(D.items * D.nsplit)), dim3(NT), 0,
+                     stream, p, D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t waves = (int64_t)D.items * HT;
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     stream, p, D);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -17,10 +17,16 @@ namespace {
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-enum class Path { None, Bf16Mfma, F32 };
+enum class Path { None, Bf16Mfma, F32, DecodeMla };
 
 Path pick_path(const cp_attn_args &a) {
   if (a.dtype == CP_BF16) {
+    // MLA-absorbed latent attention: V must be the first 512 columns of K
+    if (a.dqk == 576 && a.dv == 512)
+      return (a.v == a.k && a.v_row_stride == a.k_row_stride &&
+              a.v_head_stride == a.k_head_stride)
+                 ? Path::DecodeMla
+                 : Path::None;
     if ((a.dqk == 128 && a.dv == 128) || (a.dqk == 192 && a.dv == 128) ||
         (a.dqk == 64 && a.dv == 64))
       return Path::Bf16Mfma;
@@ -54,7 +60,15 @@ cp_status check_attn(const cp_attn_args *a) {
       if (s.pos_begin < -(1 << 29) || last > (INT32_MAX >> 1)) return CP_ERR_ARG;
     }
   }
-  if (pick_path(*a) == Path::None) return CP_ERR_UNSUPPORTED;
+  const Path path = pick_path(*a);
+  if (path == Path::None) return CP_ERR_UNSUPPORTED;
+  if (path == Path::DecodeMla) {
+    // the latent rows of a segment are addressed with 32-bit byte offsets
+    for (int32_t i = 0; i < a->num_segs; ++i) {
+      const int64_t rows = a->segs[i].kv_end - a->segs[i].kv_begin;
+      if (rows * a->k_row_stride * 2 > INT32_MAX) return CP_ERR_UNSUPPORTED;
+    }
+  }
   return CP_OK;
 }
 
@@ -139,6 +153,50 @@ std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
   return out;
 }
 
+// Decode launches: segments in chunks of kMaxLaunchSegs; the key range of
+// each (row, KV head, head block) is cut into nsplit slices so that the grid
+// covers the chip.  Returns the workspace bytes the largest launch needs.
+size_t plan_decode(const cp_attn_args &a, std::vector<DecodeLaunch> *out) {
+  const int G = a.hq / a.hkv;
+  const int htiles = (G + kDecodeHeadsPerBlock - 1) / kDecodeHeadsPerBlock;
+  size_t ws = 0;
+  std::vector<int32_t> idx;
+  for (int32_t i = 0; i < a.num_segs; ++i)
+    if (a.segs[i].q_end > a.segs[i].q_begin && a.segs[i].kv_end > a.segs[i].kv_begin)
+      idx.push_back(i);
+  for (size_t i = 0; i < idx.size(); i += kMaxLaunchSegs) {
+    DecodeLaunch D{};
+    const size_t n = std::min<size_t>(kMaxLaunchSegs, idx.size() - i);
+    int32_t items = 0, min_kv = INT32_MAX;
+    for (size_t j = 0; j < n; ++j) {
+      const cp_segment &g = a.segs[idx[i + j]];
+      SegDesc &d = D.s[j];
+      d.q_begin = g.q_begin;
+      d.q_len = g.q_end - g.q_begin;
+      d.pos_begin = g.pos_begin;
+      d.pos_stride = g.pos_stride;
+      d.kv_begin = g.kv_begin;
+      d.kv_len = g.kv_end - g.kv_begin;
+      d.tile_begin = items;
+      items += d.q_len * a.hkv * htiles;
+      min_kv = std::min(min_kv, d.kv_len);
+    }
+    // one workgroup per compute unit, slices of at least 256 keys
+    const int32_t target = 256;
+    int32_t nsplit = std::max<int32_t>(1, (target + items - 1) / items);
+    nsplit = std::min<int32_t>(nsplit, std::max<int32_t>(1, min_kv / 256));
+    D.num_segs = static_cast<int32_t>(n);
+    D.items = items;
+    D.nsplit = nsplit;
+    D.htiles = htiles;
+    D.hkv = a.hkv;
+    ws = std::max(ws, static_cast<size_t>(items) * nsplit * kDecodeHeadsPerBlock *
+                          (512 + 1) * sizeof(float));
+    if (out) out->push_back(D);
+  }
+  return ws;
+}
+
 // Rows that no kernel writes because their segment sees no KV row at all
 // (kv_end == kv_begin) still get O = 0, LSE = -inf: handled by a tiny fill.
 __global__ void fill_empty_rows(float *lse, int64_t lse_rs, void *o, int64_t o_rs,
@@ -154,6 +212,25 @@ __global__ void fill_empty_rows(float *lse, int64_t lse_rs, void *o, int64_t o_r
   else
     ((float *)o)[r * o_rs + h * o_hs + d] = 0.f;
   if (d == 0) lse[r * lse_rs + h] = -INFINITY;
+}
+
+
+// Segments that see no KV row at all get O = 0, LSE = -inf.
+cp_status fill_empty_segments(const cp_attn_args *a, hipStream_t s) {
+  for (int32_t i = 0; i < a->num_segs; ++i) {
+    const cp_segment &g = a->segs[i];
+    const int32_t n = g.q_end - g.q_begin;
+    if (n > 0 && g.kv_end == g.kv_begin) {
+      const int64_t elems = static_cast<int64_t>(n) * a->hq * a->dv;
+      hipLaunchKernelGGL(fill_empty_rows, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0,
+                         s, a->lse, a->lse_row_stride, a->o, a->o_row_stride,
+                         a->o_head_stride, a->o_dtype == CP_BF16 ? 1 : 0, a->hq, a->dv,
+                         g.q_begin, n);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return cpattn::device_error(e);
+    }
+  }
+  return CP_OK;
 }
 
 }  // namespace
@@ -188,7 +265,7 @@ extern "C" cp_status cp_attn_workspace_size(const cp_attn_args *a, size_t *bytes
   cp_status st = check_attn(a);
   if (st != CP_OK) return st;
   if (!bytes) return CP_ERR_ARG;
-  *bytes = 0;
+  *bytes = pick_path(*a) == Path::DecodeMla ? plan_decode(*a, nullptr) : 0;
   return CP_OK;
 }
 
@@ -200,28 +277,28 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const AttnParams p = make_params(*a);
   const Path path = pick_path(*a);
+  (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
+  if (path == Path::DecodeMla) {
+    std::vector<DecodeLaunch> launches;
+    const size_t need = plan_decode(*a, &launches);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return CP_ERR_SMALL_BUFFER;
+    if (need > 0 && !aligned16(a->workspace)) return CP_ERR_ARG;
+    for (DecodeLaunch &D : launches) {
+      D.ws_o = static_cast<float *>(a->workspace);
+      D.ws_lse = D.ws_o + static_cast<size_t>(D.items) * D.nsplit * kDecodeHeadsPerBlock * 512;
+      const hipError_t e = launch_attn_decode_mla(p, D, s);
+      if (e != hipSuccess) return device_error(e);
+    }
+    return fill_empty_segments(a, s);
+  }
   const int tile_rows = path == Path::F32 ? attn_f32_tile_rows(a->dqk)
                                           : attn_bf16_tile_rows(a->dqk, a->dv);
-  (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
   for (const LaunchSegs &L : plan_launches(*a, tile_rows)) {
     hipError_t e = path == Path::F32 ? launch_attn_f32(p, L, a->dqk, s)
                                      : launch_attn_bf16(p, L, a->dqk, a->dv, s);
     if (e != hipSuccess) return device_error(e);
   }
-  for (int32_t i = 0; i < a->num_segs; ++i) {
-    const cp_segment &g = a->segs[i];
-    const int32_t n = g.q_end - g.q_begin;
-    if (n > 0 && g.kv_end == g.kv_begin) {
-      const int64_t elems = static_cast<int64_t>(n) * a->hq * a->dv;
-      hipLaunchKernelGGL(fill_empty_rows, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0,
-                         s, a->lse, a->lse_row_stride, a->o, a->o_row_stride,
-                         a->o_head_stride, a->o_dtype == CP_BF16 ? 1 : 0, a->hq, a->dv,
-                         g.q_begin, n);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return device_error(e);
-    }
-  }
-  return CP_OK;
+  return fill_empty_segments(a, s);
 }
 
 extern "C" cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads,

@@ -57,6 +57,26 @@ struct AttnParams {
   int64_t ws_bytes;
 };
 
+// Decode path (MLA-absorbed shape): one workgroup per (query row, KV head,
+// block of kDecodeHeadsPerBlock query heads, key slice).  Segments travel in
+// the kernel arguments; tile_begin counts work items (q_len * hkv * htiles
+// per segment).  Slice partials go to the workspace:
+//   ws_o   fp32 [items][nsplit][kDecodeHeadsPerBlock][512]
+//   ws_lse fp32 [items][nsplit][kDecodeHeadsPerBlock]
+constexpr int kDecodeHeadsPerBlock = 128;
+
+struct DecodeLaunch {
+  int32_t num_segs;
+  int32_t items;
+  int32_t nsplit;
+  int32_t htiles;   // ceil(G / kDecodeHeadsPerBlock)
+  int32_t hkv;
+  int32_t reserved;
+  float *ws_o;
+  float *ws_lse;
+  SegDesc s[kMaxLaunchSegs];
+};
+
 // Records the HIP error for cp_last_error and returns CP_ERR_DEVICE.
 cp_status device_error(hipError_t e);
 
@@ -66,6 +86,8 @@ hipError_t launch_attn_bf16(const AttnParams &p, const LaunchSegs &L, int dqk,
                             int dv, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams &p, const LaunchSegs &L, int d,
                            hipStream_t stream);
+hipError_t launch_attn_decode_mla(const AttnParams &p, const DecodeLaunch &D,
+                                  hipStream_t stream);
 int attn_bf16_tile_rows(int dqk, int dv);
 int attn_f32_tile_rows(int d);
 

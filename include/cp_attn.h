@@ -150,9 +150,12 @@ cp_status cp_restore_index(int32_t strategy, int32_t cp_size, int32_t num_reqs,
  * (int32, num_kv_rows entries) or NULL.  workspace is device memory of at
  * least cp_attn_workspace_size bytes (NULL if that size is 0).
  *
- * Supported: dtype CP_BF16 with (dqk, dv) in {(64,64), (128,128), (192,128),
- * (576,512)} and dtype CP_F32 with dqk, dv <= 128 (multiples of 4);
- * o_dtype CP_BF16 or CP_F32; hq % hkv == 0.
+ * Supported: dtype CP_BF16 with (dqk, dv) in {(64,64), (128,128), (192,128)};
+ * dtype CP_BF16 with (dqk, dv) = (576, 512), the MLA-absorbed latent, where
+ * v must equal k with equal strides (V is the first 512 columns of each
+ * latent row) -- this path splits each row's keys into slices and needs a
+ * workspace; dtype CP_F32 with dqk = dv in {64, 128}.  o_dtype CP_BF16 or
+ * CP_F32; hq % hkv == 0.
  */
 typedef struct {
   int32_t dtype;        /* cp_dtype of q, k, v */
