@@ -35,6 +35,7 @@ def _args():
     ap.add_argument("--rank", type=int, default=0, help="CP rank whose share is timed")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="only the headline step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -206,11 +207,113 @@ def main():
             "traffic": _profiled_traffic("lse_merge_kernel<bf16,bf16>", "lse_merge.hip"),
         },
     }
-    del kv
+    del kv, o_parts, l_parts
     torch.cuda.empty_cache()
+    if not a.no_extra:
+        out["extra"] = {"zigzag_t131072_mla_direct": _direct(cp, w, q_loc, k, v, plan)}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(w, q, k, v, plan, a.cpu_baseline_seconds)
+    del q, k, v, q_loc
+    torch.cuda.empty_cache()
+    if not a.no_extra:
+        out["extra"]["zigzag_t8192_p1024"] = _prefill_ranks(cp, workloads.get("zigzag_t8192_p1024"))
+        out["extra"]["interleave_b12"] = _prefill_ranks(cp, workloads.get("interleave_b12"))
+        out["extra"]["decode_mla_b64"] = _decode(cp, workloads.get("decode_mla_b64"))
     print(json.dumps(out), flush=True)
+
+
+def _time_ms(fn, reps=5, warm=1):
+    """Average time of ``fn`` (HIP events on the current stream)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def _direct(cp, w, q_loc, k, v, plan):
+    """The same shard as one call over the full (gathered) KV."""
+    import torch
+    o = torch.empty((q_loc.shape[0], w.hq, w.dv), device=q_loc.device, dtype=torch.bfloat16)
+    lse = torch.empty((q_loc.shape[0], w.hq), device=q_loc.device, dtype=torch.float32)
+    ms = _time_ms(lambda: cp.attn_fwd(q_loc, k, v, plan, w.scale, o=o, lse=lse), reps=3)
+    fl = _useful_flops(_rank_pairs(plan), w.hq, w.dqk, w.dv)
+    return {"ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
+            "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
+def _prefill_ranks(cp, w):
+    """Each rank's shard of a prefill workload against the gathered KV:
+    per-rank time and useful TFLOP/s, and all ranks back to back."""
+    import numpy as np
+    import torch
+    import workloads
+    q, k, v = workloads.prefill_tensors(w, "cuda")
+    lens, pre = list(w.new_lens), list(w.prefix_lens)
+    ranks = []
+    total_fl, total_ms = 0.0, 0.0
+    for r in range(w.cp_size):
+        plan = cp.shard_plan(w.strategy, w.cp_size, r, lens, pre)
+        q_loc = q.index_select(0, torch.from_numpy(plan.global_idx.astype(np.int64)).cuda())
+        o = torch.empty((plan.num_local, w.hq, w.dv), device="cuda", dtype=q.dtype)
+        lse = torch.empty((plan.num_local, w.hq), device="cuda", dtype=torch.float32)
+        ms = _time_ms(lambda: cp.attn_fwd(q_loc, k, v, plan, w.scale, o=o, lse=lse), reps=10)
+        fl = _useful_flops(_rank_pairs(plan), w.hq, w.dqk, w.dv)
+        total_fl += fl
+        total_ms += ms
+        ranks.append({"rank": r, "ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1)})
+    return {"ranks": ranks, "all_ranks_ms": round(total_ms, 4),
+            "all_ranks_TFLOP/s": round(total_fl / total_ms / 1e9, 1),
+            "frac_bf16_peak": round(total_fl / total_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
+def _decode(cp, w):
+    """Decode-CP: each of the W token-interleaved KV shards (fp32 partials),
+    then the LSE merge.  HBM-bound: algorithmic bytes = the shard's latent
+    rows + q + the fp32 partial output and its LSE."""
+    import numpy as np
+    import torch
+    import workloads
+    q, kv = workloads.decode_tensors(w, "cuda")
+    W, B, ctx = w.cp_size, w.num_reqs, w.ctx_len
+    shards = [kv[:, j::W].contiguous() for j in range(W)]
+    del kv
+    torch.cuda.empty_cache()
+    n_j = ctx // W
+    o_parts = torch.empty((W, B, w.hq, w.dv), device="cuda", dtype=torch.float32)
+    l_parts = torch.empty((W, B, w.hq), device="cuda", dtype=torch.float32)
+    segs = [cp.Segment(b, b, b + 1, ctx, 1, b * n_j, (b + 1) * n_j) for b in range(B)]
+    ws = None
+    res = []
+    for j, sh in enumerate(shards):
+        k = sh.view(B * n_j, 1, w.dqk)
+        vv = k[:, :, :w.dv]
+        pos = torch.arange(j, ctx, W, device="cuda", dtype=torch.int32).repeat(B)
+        if ws is None:
+            a, keep = cp._lib.attn_args(q, k, vv, segs, w.scale, o_parts[j], l_parts[j],
+                                        kv_pos=pos)
+            ws = torch.empty(cp.attn_workspace_size(a), device="cuda", dtype=torch.uint8)
+        ms = _time_ms(lambda: cp.attn_fwd(q, k, vv, segs, w.scale, kv_pos=pos, o=o_parts[j],
+                                          lse=l_parts[j], workspace=ws), reps=10)
+        res.append(ms)
+    by = B * n_j * w.dqk * 2 + q.numel() * 2 + B * w.hq * (w.dv * 4 + 4)
+    o_out = torch.empty((B, w.hq, w.dv), device="cuda", dtype=torch.bfloat16)
+    l_out = torch.empty((B, w.hq), device="cuda", dtype=torch.float32)
+    mms = _time_ms(lambda: cp.lse_merge(o_parts, l_parts, o_out=o_out, lse_out=l_out), reps=10)
+    mby = W * B * w.hq * (w.dv * 4 + 4) + B * w.hq * (w.dv * 2 + 4)
+    ms = float(np.mean(res))
+    fl = 2.0 * B * w.hq * n_j * (w.dqk + w.dv)
+    return {"shard_ms": round(ms, 4), "algorithmic_bytes_per_shard": by,
+            "GB/s": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "TFLOP/s": round(fl / ms / 1e9, 1), "workspace_bytes": int(ws.numel()),
+            "merge_ms": round(mms, 4), "merge_GB/s": round(mby / mms / 1e6, 1),
+            "merge_frac_hbm": round(mby / mms / 1e6 / PEAK_HBM_GBS, 4),
+            "merge_note": "the partials (134 MB) fit the 256 MB Infinity Cache: effective rate"}
 
 
 def _cpu_baseline(w, q, k, v, plan, budget_s):

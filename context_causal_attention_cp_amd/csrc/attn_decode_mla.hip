@@ -86,6 +86,22 @@ __device__ inline float sum_groups(float x) {
   return x + __shfl_xor(x, 32, 64);
 }
 
+// ds_read_b64_tr_b16 through inline asm.  The intrinsic makes the waitcnt pass
+// assume it may alias the LDS-DMA writes still in flight and drain them
+// (vmcnt(0)) before every use; the tile it reads was already completed by
+// an explicit vmcnt wait and a barrier.  Results are consumed only after
+// lds_wait(), which ties them to an lgkmcnt(0) by a data dependency.
+__device__ inline u32x2 lds_read_tr16(const void *p) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1"
+               : "=v"(r)
+               : "v"((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p));
+  return r;
+}
+__device__ inline void lds_wait(u32x2 &a, u32x2 &b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+
 // vmcnt wait with the other counters left alone (gfx9 encoding)
 template <int N>
 __device__ inline void wait_vm() {
@@ -110,7 +126,8 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
   __shared__ __attribute__((aligned(1024))) u32x4 sk[NBUF][TILE_CH];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int item = blockIdx.x / D.nsplit, split = blockIdx.x % D.nsplit;
   if (item >= D.items) return;
   int si, row, kvh, ht;
@@ -197,19 +214,22 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
   //  The swizzle only depends on key bits 0..3, so key + 16 is the same read
   //  shifted by 16 rows (kRow16 bytes).
   constexpr int kRow16 = 16 * KCH * 16;
-  int qk_base[2];
-#pragma unroll
-  for (int odd = 0; odd < 2; ++odd) qk_base[odd] = 16 * (n * KCH + ((4 * odd + g) ^ swz(n)));
   //  transposing reads (PV): lane li of group g addresses key 4g + li/4 (+16),
   //  dv 16*b + 4*(li%4): chunk 2*b + (li%4)/2 = 8*(b>>2) + (2*(b&3) + (li%4)/2),
-  //  byte 8*(li&1) inside the chunk
-  int tr_base[4];
-  {
-    const int key = 4 * g + (n >> 2);
+  //  byte 8*(li&1) inside the chunk.
+  //  The bases are rebuilt every tile from an opaque copy of the lane id (a
+  //  few integer ops) rather than kept live across the loop.
+  auto lds_bases = [&](int (&qk_base)[2], int (&tr_base)[4]) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int nn = ln & 15, gg = ln >> 4;
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) qk_base[odd] = 16 * (nn * KCH + ((4 * odd + gg) ^ swz(nn)));
+    const int key = 4 * gg + (nn >> 2);
 #pragma unroll
     for (int b4 = 0; b4 < 4; ++b4)
-      tr_base[b4] = 16 * (key * KCH + ((2 * b4 + ((n & 3) >> 1)) ^ swz(key))) + 8 * (n & 1);
-  }
+      tr_base[b4] = 16 * (key * KCH + ((2 * b4 + ((nn & 3) >> 1)) ^ swz(key))) + 8 * (nn & 1);
+  };
 
   if (ntiles > 0) issue(0);
   if (ntiles > 1) issue(1);
@@ -223,6 +243,8 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
     if (t + 2 < ntiles) issue(t + 2);
     const char *tile = (const char *)sk[t % NBUF];
     const int j0 = k_lo + t * BN;
+    int qk_base[2], tr_base[4];
+    lds_bases(qk_base, tr_base);
 
     // ---- S^T = K Q^T : two 16-key blocks x 16 heads
     f32x4 s[2];
@@ -267,28 +289,34 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
     float ls = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const float p0 = exp2f(s[mb][0] - m_use), p1 = exp2f(s[mb][1] - m_use);
-      const float p2 = exp2f(s[mb][2] - m_use), p3 = exp2f(s[mb][3] - m_use);
+      const float p0 = __builtin_amdgcn_exp2f(s[mb][0] - m_use), p1 = __builtin_amdgcn_exp2f(s[mb][1] - m_use);
+      const float p2 = __builtin_amdgcn_exp2f(s[mb][2] - m_use), p3 = __builtin_amdgcn_exp2f(s[mb][3] - m_use);
       ls += (p0 + p1) + (p2 + p3);
       pk[2 * mb] = pack_bf16(p0, p1);
       pk[2 * mb + 1] = pack_bf16(p2, p3);
     }
     l_run += ls;
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
-    // ---- O^T += V^T P^T : V^T from the same tile by transposing reads
+    // ---- O^T += V^T P^T : V^T from the same tile by transposing reads, in
+    // batches of 4 dv blocks
+    constexpr int PB = 4;
 #pragma unroll
-    for (int b = 0; b < OB; ++b) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4 *)(tile + tr_base[b & 3] + 128 * (b >> 2)));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4 *)(tile + tr_base[b & 3] + kRow16 + 128 * (b >> 2)));
-      // whole-vector bit casts: building the operand element by element from
-      // the 16-bit lanes of the transposing reads miscompiles (every element
-      // becomes element 0)
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
-      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-      oacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[b], 0, 0, 0);
+    for (int b0 = 0; b0 < OB; b0 += PB) {
+      u32x2 vl[PB], vh[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const int b = b0 + j;
+        vl[j] = lds_read_tr16(tile + tr_base[b & 3] + 128 * (b >> 2));
+        vh[j] = lds_read_tr16(tile + tr_base[b & 3] + kRow16 + 128 * (b >> 2));
+      }
+#pragma unroll
+      for (int j = 0; j < PB; ++j) lds_wait(vl[j], vh[j]);
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const u32x4 av = {vl[j][0], vl[j][1], vh[j][0], vh[j][1]};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+        oacc[b0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[b0 + j], 0, 0, 0);
+      }
     }
   }
 

@@ -8,25 +8,28 @@
 // whose position is <= the row's position, and LSE = ln sum exp(scale q k).
 // Query head h reads KV head h / (hq/hkv) (GQA, blog section 4.1).
 //
-// Structure of one workgroup (4 waves, 256 threads):
-//   * a tile of 128 query rows of one segment and one query head; wave w
-//     owns rows 32w..32w+31 and keeps their Q fragments in registers;
-//   * the keys are visited in tiles of 64: K and V of the tile are staged in
-//     LDS (V transposed, see below), the next tile's global loads are in
-//     flight while the current one is computed;
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with keys as the M dimension
-//     and query rows as N, so every lane holds scores of ONE query row
-//     (lane % 32) for 32 of the 64 keys; the row max and the exponentials
-//     stay lane-local except for one exchange with lane ^ 32;
-//   * online softmax in fp32 with exp2 and scale*log2(e) folded in;
-//   * O^T += V^T P^T on the same MFMA with dv as M, keys as the contraction
-//     and query rows as N: P leaves the score registers as the B operand
-//     with no data movement, because the MFMA's B layout (lane % 32 = column)
-//     matches the accumulator layout of S^T.  The contraction order of the
-//     keys inside each 16-key step is the accumulator's order; V^T is stored
-//     in LDS in that same order, so its A operand is one 16-byte LDS read.
-//   * tiles are classified per wave from their endpoint positions: fully
-//     visible (no mask), fully hidden (skipped), or on the diagonal (mask).
+// One workgroup = 4 waves = 256 query rows of one segment and one head; each
+// wave owns 64 rows (two 32-row MFMA column blocks), one wave per SIMD:
+//   * K and V tiles of 64 keys are copied HBM -> LDS by range-checked buffer
+//     loads straight into XOR-swizzled tiles (no register staging), three
+//     stages in flight;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, query rows = N): each
+//     lane holds scores of one query row, so the softmax is lane-local; the
+//     Q fragments stay in registers; every K fragment read from LDS feeds two
+//     MFMAs (both row blocks);
+//   * O^T += V^T P^T: P leaves the score registers as the B operand; V^T is
+//     read from the row-major V tile with the transposing LDS read
+//     ds_read_b64_tr_b16, in the accumulator's key order;
+//   * exp2 with scale*log2(e) folded into one FMA; the reference max of a row
+//     only moves (with an accumulator rescale) when the row outgrows it by
+//     more than 2^8;
+//   * per wave, the number of visible tiles and of fully visible tiles is
+//     counted once up front from the tiles' first/last key positions (one
+//     wave-wide vector load per 64 tiles); only boundary tiles are masked;
+//   * O is transposed through LDS and written as whole rows.
+// Work mapping: all workgroups of one KV head go to one XCD (id mod 8) so the
+// ones streaming the same K/V share that XCD's L2; inside a head the
+// heaviest tiles (longest causal extent) start first.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -38,21 +41,20 @@ namespace cpattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128;   // query rows per workgroup
-constexpr int BN = 64;    // keys per tile
-constexpr int NT = 256;   // threads
+constexpr int NW = 4;          // waves
+constexpr int NT = 64 * NW;    // threads
+constexpr int RW = 64;         // query rows per wave
+constexpr int BM = RW * NW;    // query rows per workgroup
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kNoPos = -(1 << 30);  // position of a padding row: sees nothing
+constexpr float kRescale = 8.0f;
+constexpr int kNoPos = -(1 << 30);
 
-__device__ inline void map_work(int id, int num_tiles, int hq, int hkv,
-                                int &tile_order, int &h) {
-  // All work of one KV head goes to one XCD queue (id % 8) so that the
-  // workgroups streaming the same K/V share that XCD's L2; within a KV head
-  // the heaviest tiles come first.
+__device__ inline void map_work(int id, int num_tiles, int hq, int hkv, int &tile_order, int &h) {
   const int G = hq / hkv;
   const int per_kvh = num_tiles * G;
   int kvh, rem;
@@ -75,264 +77,474 @@ __device__ inline int find_seg(const LaunchSegs &L, int tile_order) {
   return si;
 }
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
 __device__ inline uint32_t pack_bf16(float a, float b) {
   const __bf16 lo = (__bf16)a, hi = (__bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
          ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
+__device__ inline float max_xor32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ inline float sum_xor32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// ds_read_b64_tr_b16 through inline asm.  The intrinsic makes the waitcnt pass
+// assume it may alias the LDS-DMA writes still in flight and drain them
+// (vmcnt(0)) before every use; the tile it reads was already completed by
+// an explicit vmcnt wait and a barrier.  Results are consumed only after
+// lds_wait(), which ties them to an lgkmcnt(0) by a data dependency.
+__device__ inline u32x2 lds_read_tr16(const void *p) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1"
+               : "=v"(r)
+               : "v"((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p));
+  return r;
+}
+__device__ inline void lds_wait(u32x2 &a, u32x2 &b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait until at most `later` tiles of PER instructions each are outstanding
+// (later <= MAXL, uniform)
+template <int PER, int MAXL>
+__device__ inline void wait_later(int later) {
+  if constexpr (MAXL >= 5) if (later >= 5) { wait_vm<5 * PER>(); return; }
+  if constexpr (MAXL >= 4) if (later == 4) { wait_vm<4 * PER>(); return; }
+  if constexpr (MAXL >= 3) if (later == 3) { wait_vm<3 * PER>(); return; }
+  if constexpr (MAXL >= 2) if (later == 2) { wait_vm<2 * PER>(); return; }
+  if constexpr (MAXL >= 1) if (later == 1) { wait_vm<PER>(); return; }
+  wait_vm<0>();
+}
+
+// XOR swizzles of the 16-byte chunk index inside a tile row (key bits k0..k3).
+//  K rows are read as 16 consecutive keys at one chunk: with 8 mod 16 chunks
+//  per row the swizzle is (k0^k3) | (k0^k1)<<1 | (k0^k2)<<2 (inside aligned
+//  groups of 8 chunks); with 16 chunks per row it is the key's low 4 bits.
+//  V rows are read transposed, 4 consecutive keys x 4 chunks: key bits 0,1 go
+//  to chunk bits 1,2 (and 3).  Both keep those reads free of bank conflicts
+//  for 32- and 64-bank LDS.
+template <int KCH>
+__device__ inline int kswz(int key) {
+  if constexpr (KCH % 16 == 0) {
+    return key & 15;
+  } else {
+    const int k0 = key & 1, k1 = (key >> 1) & 1, k2 = (key >> 2) & 1, k3 = (key >> 3) & 1;
+    return (k0 ^ k3) | ((k0 ^ k1) << 1) | ((k0 ^ k2) << 2);
+  }
+}
+template <int VCH>
+__device__ inline int vswz(int key) {
+  const int k0 = key & 1, k1 = (key >> 1) & 1;
+  if constexpr (VCH % 16 == 0) return (k0 << 1) | (k1 << 2) | (k0 << 3);
+  else return (k0 << 1) | (k1 << 2);
+}
+
+// Tile width and LDS stages per head-dim pair: 64-key tiles and 3 stages
+// where registers allow; 32-key tiles and 6 stages (five tiles prefetched)
+// for the 192-wide K, whose Q fragments need 96 registers.
 template <int DQK, int DV>
-struct Smem {
-  static constexpr int KP = DQK + 8;  // K row pitch (elements), 16B aligned
-  static constexpr int VP = BN + 8;   // V^T row pitch (elements)
-  __bf16 k[BN * KP];
-  __bf16 vt[DV * VP];
-  int kpos[BN];
+struct Cfg {
+  static constexpr int BN = DQK > 128 ? 32 : 64;   // keys per tile
+  static constexpr int NBUF = DQK > 128 ? 6 : 3;   // LDS stages
+  static constexpr int NKB_ = BN / 32;             // 32-key blocks per tile
+  static constexpr int KSTEP = BN / 16;            // 16-key PV steps per tile
+  static constexpr int KCH = DQK / 8;          // 16-byte chunks per K row
+  static constexpr int VCH = DV / 8;           // ... per V row
+  static constexpr int KTILE = BN * KCH;       // chunks per K tile
+  static constexpr int KPOS = BN * (KCH + VCH);  // key positions after K and V
+  static constexpr int STAGE = KPOS + BN / 4;
+  static constexpr int KDMA = BN * KCH / 64 / NW;  // K DMA instructions per wave per stage
+  static constexpr int VDMA = BN * VCH / 64 / NW;
+  static constexpr int KS = DQK / 16;          // QK k-steps
+  static constexpr int OB = DV / 32;           // 32-row dv blocks
+  static_assert((BN * KCH / 64) % NW == 0 && (BN * VCH / 64) % NW == 0, "DMA split");
+  static_assert(KCH % 8 == 0 && VCH % 8 == 0, "swizzle groups");
 };
 
 template <int DQK, int DV>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT),
-                          amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
-  static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
-  constexpr int KP = Smem<DQK, DV>::KP;
-  constexpr int VP = Smem<DQK, DV>::VP;
-  constexpr int KCH = DQK / 8;              // 16B chunks per K row
-  constexpr int KLD = (BN * KCH) / NT;      // K chunks per thread
-  static_assert((BN * KCH) % NT == 0, "K staging");
-  constexpr int VPAIRS = (BN / 4) * (DV / 8);  // (4 keys x 8 dv) groups
-  static_assert(VPAIRS <= NT, "V staging");
-  constexpr int QS = DQK / 16;              // MFMA k-steps for S
-  constexpr int OB = DV / 32;               // 32-wide dv blocks of O
-
-  __shared__ __attribute__((aligned(16))) Smem<DQK, DV> sm;
+  using C = Cfg<DQK, DV>;
+  constexpr int KCH = C::KCH, VCH = C::VCH, KS = C::KS, OB = C::OB;
+  constexpr int BN = C::BN, NBUF = C::NBUF, NKBLK = C::NKB_, KSTEP = C::KSTEP;
+  __shared__ __attribute__((aligned(1024))) u32x4 sm[C::NBUF][C::STAGE];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, n = lane & 31, hf = lane >> 5;
+  // the wave index is uniform per wave: say so, so that everything derived
+  // from it (tile counts, DMA slots) stays in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, n = lane & 31, hf = lane >> 5;
 
   int tile_order, h;
   map_work(blockIdx.x, L.num_tiles, p.hq, p.hkv, tile_order, h);
   if (tile_order >= L.num_tiles) return;
   const SegDesc sd = L.s[find_seg(L, tile_order)];
-  const int ntile = (sd.q_len + BM - 1) / BM;
-  const int t = ntile - 1 - (tile_order - sd.tile_begin);
-  const int row0 = t * BM;
+  const int ntile_q = (sd.q_len + BM - 1) / BM;
+  const int tq = ntile_q - 1 - (tile_order - sd.tile_begin);
+  const int row0 = tq * BM;
   const int rows_here = min(BM, sd.q_len - row0);
   const int kvh = h / (p.hq / p.hkv);
 
-  // ---- this lane's query row
-  const int rr = w * 32 + n;
-  const bool valid = rr < rows_here;
-  const int64_t qrow = (int64_t)sd.q_begin + row0 + rr;
-  const int qpos = valid ? sd.pos_begin + (row0 + rr) * sd.pos_stride : kNoPos;
-  const int nvalid_w = max(0, min(32, rows_here - w * 32));
-  const int qmin_w = nvalid_w ? sd.pos_begin + (row0 + w * 32) * sd.pos_stride : kNoPos;
+  // ---- this lane's two query rows (row blocks rb = 0, 1)
+  int qpos[2];
+  bool valid[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int rr = w * RW + rb * 32 + n;
+    valid[rb] = rr < rows_here;
+    qpos[rb] = valid[rb] ? sd.pos_begin + (row0 + rr) * sd.pos_stride : kNoPos;
+  }
+  const int nvalid_w = max(0, min(RW, rows_here - w * RW));
+  const int qmin_w = nvalid_w ? sd.pos_begin + (row0 + w * RW) * sd.pos_stride : kNoPos;
   const int qmax_w =
-      nvalid_w ? sd.pos_begin + (row0 + w * 32 + nvalid_w - 1) * sd.pos_stride : kNoPos;
+      nvalid_w ? sd.pos_begin + (row0 + w * RW + nvalid_w - 1) * sd.pos_stride : kNoPos;
   const int qmax_wg = sd.pos_begin + (row0 + rows_here - 1) * sd.pos_stride;
 
-  bf16x8 qf[QS];
-  {
+  // ---- tile counts: visible for the workgroup / this wave, fully visible
+  const int n_kv = sd.kv_len;
+  const int ntiles_all = (n_kv + BN - 1) / BN;
+  const int32_t *kvp = p.kv_pos ? p.kv_pos + sd.kv_begin : nullptr;
+  int n_wg, n_vis, n_full;
+  if (!p.causal) {
+    n_wg = n_vis = ntiles_all;
+    n_full = n_kv / BN;
+  } else if (!kvp) {
+    n_wg = (min(n_kv, max(qmax_wg + 1, 0)) + BN - 1) / BN;
+    n_vis = (min(n_kv, max(qmax_w + 1, 0)) + BN - 1) / BN;
+    n_full = min(n_kv, max(qmin_w + 1, 0)) / BN;
+  } else {
+    // positions increase: count tiles whose first key is visible to the
+    // last row, and tiles whose last key is visible to the first row
+    n_wg = n_vis = n_full = 0;
+    for (int t0 = 0; t0 < ntiles_all; t0 += 64) {
+      const int t = t0 + lane;
+      int first = INT_MAX, last = INT_MAX;
+      if (t < ntiles_all) {
+        first = kvp[t * BN];
+        if ((t + 1) * BN <= n_kv) last = kvp[t * BN + BN - 1];
+      }
+      n_wg += __builtin_popcountll(__builtin_amdgcn_ballot_w64(first <= qmax_wg));
+      n_vis += __builtin_popcountll(__builtin_amdgcn_ballot_w64(first <= qmax_w));
+      n_full += __builtin_popcountll(__builtin_amdgcn_ballot_w64(last <= qmin_w));
+    }
+  }
+  if (nvalid_w == 0) n_vis = n_full = 0;
+
+  // ---- Q fragments: B operand of S^T = K Q^T (n = row, k = d)
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int64_t qrow = (int64_t)sd.q_begin + row0 + w * RW + rb * 32 + n;
     const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)h * p.q_hs + 8 * hf;
 #pragma unroll
-    for (int s = 0; s < QS; ++s) {
+    for (int s = 0; s < KS; ++s) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (valid) x = *(const u32x4 *)(qp + 16 * s);
-      qf[s] = __builtin_bit_cast(bf16x8, x);
+      if (valid[rb]) x = *(const u32x4 *)(qp + 16 * s);
+      qf[rb][s] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  const int n_kv = sd.kv_len;
-  const int32_t *kvp = p.kv_pos ? p.kv_pos + sd.kv_begin : nullptr;
-  auto key_pos = [&](int j) -> int { return kvp ? kvp[j] : j; };
-  auto tile_live = [&](int j0) -> bool {
-    return j0 < n_kv && (!p.causal || key_pos(j0) <= qmax_wg);
-  };
-
+  // ---- LDS DMA of one stage: K rows then V rows of keys [j0, j0 + 64)
   const __bf16 *kbase = (const __bf16 *)p.k + (int64_t)sd.kv_begin * p.k_rs + (int64_t)kvh * p.k_hs;
   const __bf16 *vbase = (const __bf16 *)p.v + (int64_t)sd.kv_begin * p.v_rs + (int64_t)kvh * p.v_hs;
-
-  // ---- staging registers for the next tile
-  u32x4 kreg[KLD];
-  u32x4 vreg[4];
-  int preg = INT_MAX;
-  const int vdc = tid / 16, vkc = tid % 16;  // V group: dv 8*vdc.., keys 4*vkc..
-  const bool vthread = tid < VPAIRS;
-
-  auto load_tile = [&](int j0) {
+  auto issue = [&](int t) {
+    const int j0 = t * BN;
+    const int nrows = min(BN, n_kv - j0);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(kbase + (int64_t)j0 * p.k_rs), (short)0, (int)(nrows * p.k_rs * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(vbase + (int64_t)j0 * p.v_rs), (short)0, (int)(nrows * p.v_rs * 2), 0x00020000);
+    u32x4 *dst = sm[t % NBUF];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recomputed per stage, not kept live
 #pragma unroll
-    for (int c = 0; c < KLD; ++c) {
-      const int ch = tid + NT * c;
-      const int kr = ch / KCH, kc = ch % KCH;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (j0 + kr < n_kv) x = *(const u32x4 *)(kbase + (int64_t)(j0 + kr) * p.k_rs + kc * 8);
-      kreg[c] = x;
+    for (int i = 0; i < C::KDMA; ++i) {
+      const int slot = (w * C::KDMA + i) * 64 + ln;
+      const int key = slot / KCH, cs = slot % KCH;
+      const uint32_t off = (uint32_t)(key * p.k_rs + (cs ^ kswz<KCH>(key)) * 8) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          kr, (__attribute__((address_space(3))) void *)(dst + (w * C::KDMA + i) * 64), 16, off,
+          0, 0, 0);
     }
-    if (vthread) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + vkc * 4 + i;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (j < n_kv) x = *(const u32x4 *)(vbase + (int64_t)j * p.v_rs + vdc * 8);
-        vreg[i] = x;
-      }
+    for (int i = 0; i < C::VDMA; ++i) {
+      const int slot = (w * C::VDMA + i) * 64 + ln;
+      const int key = slot / VCH, cs = slot % VCH;
+      const uint32_t off = (uint32_t)(key * p.v_rs + (cs ^ vswz<VCH>(key)) * 8) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vr, (__attribute__((address_space(3))) void *)(dst + C::KTILE + (w * C::VDMA + i) * 64),
+          16, off, 0, 0, 0);
     }
-    if (tid < BN) preg = (j0 + tid < n_kv) ? key_pos(j0 + tid) : INT_MAX;
+    if (kvp && w == 0 && ln < BN) {
+      const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(kvp + j0), (short)0, nrows * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          pr, (__attribute__((address_space(3))) void *)(dst + C::KPOS), 4, (uint32_t)ln * 4u, 0,
+          0, 0);
+    }
   };
 
-  auto store_tile = [&]() {
+  // per-lane LDS byte offsets: K row reads (key 32*nb + n, chunk 2*s + hf =
+  // 8*(s>>2) + (2*(s&3) + hf)), V transposing reads (key 16*ks + 4*hf + li/4
+  // (+8), dv 32*mb + 16*(blk&1) + 4*(li&3)).  They are rebuilt every tile
+  // from an opaque copy of the lane id (a few integer ops) rather than kept
+  // live across the loop.
+  constexpr int kKeyBytes = KCH * 16;
+  // 3-bit swizzle: chunk 2*s + hf = 8*(s>>2) + (2*(s&3) + hf) -> 4 bases + an
+  // immediate; 4-bit swizzle (16-chunk rows): one base per k-step
+  constexpr bool kSw4 = (KCH % 16 == 0);
+  constexpr int NKB = kSw4 ? KS : 4;
+  auto lds_bases = [&](int (&kbo)[NKB], int (&vbo)[OB]) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int nn = ln & 31, hh = ln >> 5, lli = ln & 15, bb = ln >> 4;
 #pragma unroll
-    for (int c = 0; c < KLD; ++c) {
-      const int ch = tid + NT * c;
-      const int kr = ch / KCH, kc = ch % KCH;
-      *(u32x4 *)&sm.k[kr * KP + kc * 8] = kreg[c];
-    }
-    if (vthread) {
-      // 4 keys x 8 dv -> for each dv, the 4 keys as one 8-byte LDS write.
-      // Keys go to the accumulator order of a 16-key MFMA step: the 4-key
-      // chunks 0,1,2,3 of each 16 keys are stored at chunk slots 0,2,1,3.
-      const int g16 = vkc >> 2, c4 = vkc & 3;
-      const int slot = g16 * 16 + (((c4 & 1) << 1) | (c4 >> 1)) * 4;
+    for (int s4 = 0; s4 < NKB; ++s4) kbo[s4] = 16 * (nn * KCH + ((2 * s4 + hh) ^ kswz<KCH>(nn)));
+    const int vkey = 4 * hh + (lli >> 2);
 #pragma unroll
-      for (int d2 = 0; d2 < 4; ++d2) {
-        const uint32_t a0 = vreg[0][d2], a1 = vreg[1][d2], a2 = vreg[2][d2], a3 = vreg[3][d2];
-        u32x2 lo, hi;  // dv = 2*d2 (low halves) and 2*d2+1 (high halves)
-        lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-        hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-        hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-        const int dv0 = vdc * 8 + 2 * d2;
-        *(u32x2 *)&sm.vt[dv0 * VP + slot] = lo;
-        *(u32x2 *)&sm.vt[(dv0 + 1) * VP + slot] = hi;
-      }
+    for (int mb = 0; mb < OB; ++mb) {
+      const int chunk = 4 * mb + 2 * (bb & 1) + ((lli & 3) >> 1);
+      vbo[mb] = C::KTILE * 16 + 16 * (vkey * VCH + (chunk ^ vswz<VCH>(vkey))) + 8 * (lli & 1);
     }
-    if (tid < BN) sm.kpos[tid] = preg;
   };
 
-  f32x16 oacc[OB];
+  f32x16 oacc[OB][2];
 #pragma unroll
   for (int b = 0; b < OB; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[b][i] = 0.f;
-  float m_run = -INFINITY;  // running max (log2 units), same in both halves
-  float l_run = 0.f;        // this half's partial row sum
-
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[b][rb][i] = 0.f;
+  float m_ref[2] = {-INFINITY, -INFINITY};  // reference max (log2 units) per row block
+  float l_run[2] = {0.f, 0.f};              // this half's partial row sums
   const float sl2 = p.scale_log2;
-  int j0 = 0;
-  bool live = tile_live(0);
-  if (live) load_tile(0);
-  while (live) {
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    const int jn = j0 + BN;
-    const bool live_next = tile_live(jn);
-    if (live_next) load_tile(jn);
 
-    // classify this tile for this wave
-    const int jlast = min(j0 + BN, n_kv) - 1;
-    const int kmin = sm.kpos[0];
-    const int kmax = sm.kpos[jlast - j0];
-    const bool hidden = nvalid_w == 0 || (p.causal && kmin > qmax_w);
-    const bool full = (j0 + BN <= n_kv) && (!p.causal || kmax <= qmin_w);
-    if (!hidden) {
-      f32x16 s[2];
+  // S^T = K Q^T for one tile: 2 key blocks x 2 row blocks
+  auto qk_tile = [&](f32x16 (&sc)[NKBLK][2], const char *tl, const int (&kbi)[NKB]) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NKBLK; ++nb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
-        const __bf16 *kp = &sm.k[(32 * nb + n) * KP + 8 * hf];
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int st = 0; st < QS; ++st) {
-          const bf16x8 a = *(const bf16x8 *)(kp + 16 * st);
-          s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[nb], 0, 0, 0);
-        }
+        for (int i = 0; i < 16; ++i) sc[nb][rb][i] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NKBLK; ++nb) {
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const int koff = kSw4 ? kbi[st] : kbi[st & 3] + 128 * (st >> 2);
+        const bf16x8 a = *(const bf16x8 *)(tl + koff + 32 * nb * kKeyBytes);
+        sc[nb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][st], sc[nb][0], 0, 0, 0);
+        sc[nb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][st], sc[nb][1], 0, 0, 0);
       }
-      // scores -> log2 units, mask, row max
-      float mx = -INFINITY;
+    }
+  };
+  // mask on boundary tiles; lane-local row max (log2 units) per row block
+  auto mask_and_max = [&](f32x16 (&sc)[NKBLK][2], float (&m2)[2], int tt, int jj0) {
+    if (tt >= n_full) {
+      const int *kp = (const int *)(sm[tt % NBUF] + C::KPOS);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NKBLK; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float u = s[nb][i] * sl2;
-          if (!full) {
-            const int kj = 32 * nb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            const bool vis = (j0 + kj < n_kv) && (!p.causal || sm.kpos[kj] <= qpos);
-            u = vis ? u : -INFINITY;
+          const int kj = 32 * nb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          const int kpos = kvp ? kp[kj] : jj0 + kj;
+          const bool in = jj0 + kj < n_kv;
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const bool vis = in && (!p.causal || kpos <= qpos[rb]);
+            sc[nb][rb][i] = vis ? sc[nb][rb][i] : -INFINITY;
           }
-          s[nb][i] = u;
-          mx = fmaxf(mx, u);
         }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      m_run = m_new;
-      float ls = 0.f;
-      bf16x8 pf[4];
+    }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+    for (int rb = 0; rb < 2; ++rb) {
+      float m = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          u32x4 pk;
+      for (int nb = 0; nb < NKBLK; ++nb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = exp2f(s[nb][8 * c + 2 * e] - m_use);
-            const float p1 = exp2f(s[nb][8 * c + 2 * e + 1] - m_use);
-            ls += p0 + p1;
-            pk[e] = pack_bf16(p0, p1);
-          }
-          pf[2 * nb + c] = __builtin_bit_cast(bf16x8, pk);
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[nb][rb][i]);
+      m2[rb] = m * sl2;
+    }
+  };
+  // per 16-key step: P = exp2(s*scale*log2e - m) packed as the B operand,
+  // then O^T += V^T P^T with V^T from transposing reads shared by both row
+  // blocks (P is made just before use to keep few registers live)
+  auto pv_tile = [&](f32x16 (&sc)[NKBLK][2], const char *tl, const int (&vbi)[OB]) {
+    float mneg[2], ls[2] = {0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) mneg[rb] = (m_ref[rb] == -INFINITY) ? 0.f : -m_ref[rb];
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) {
+      const int nb = ks >> 1, c = ks & 1;
+      // V^T fragments of this step (transposing reads), shared by both row
+      // blocks; issued first so the exponentials below hide their latency
+      u32x2 vl[OB], vh[OB];
+#pragma unroll
+      for (int b = 0; b < OB; ++b) {
+        const char *vp = tl + vbi[b] + 16 * ks * VCH * 16;
+        vl[b] = lds_read_tr16(vp);
+        vh[b] = lds_read_tr16(vp + 8 * VCH * 16);
+      }
+      bf16x8 pf[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[nb][rb][8 * c + 2 * e], sl2, mneg[rb]));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[nb][rb][8 * c + 2 * e + 1], sl2, mneg[rb]));
+          ls[rb] += p0 + p1;
+          pk[e] = pack_bf16(p0, p1);
         }
-      l_run = l_run * alpha + ls;
+        pf[rb] = __builtin_bit_cast(bf16x8, pk);
+      }
+#pragma unroll
+      for (int b = 0; b < OB; ++b) lds_wait(vl[b], vh[b]);
+#pragma unroll
+      for (int b = 0; b < OB; ++b) {
+        const u32x4 av = {vl[b][0], vl[b][1], vh[b][0], vh[b][1]};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+        oacc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0], oacc[b][0], 0, 0, 0);
+        oacc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1], oacc[b][1], 0, 0, 0);
+      }
+    }
+    l_run[0] += ls[0];
+    l_run[1] += ls[1];
+  };
+
+  constexpr int PREF = NBUF - 1;  // tiles in flight ahead of the one computed
+#pragma unroll
+  for (int i = 0; i < PREF; ++i)
+    if (i < n_wg) issue(i);
+  constexpr int DMA_W = C::KDMA + C::VDMA;
+
+  // The tile loop.  The hot path never rescales the accumulator: the first
+  // visible tile of a row only sets its reference max (O and l are still
+  // zero), and a later growth beyond the headroom leaves the loop for the
+  // cold path below, which rescales and then finishes that tile.
+  int t = 0;
+  f32x16 s[NKBLK][2];
+  float mx[2];
+  const char *tile = nullptr;
+  int j0 = 0;
+  int vbi[OB];
+  while (true) {
+    bool need_rescale = false;
+    for (; t < n_wg; ++t) {
+      t = __builtin_amdgcn_readfirstlane(t);  // uniform loop counter
+      // tile t's DMA is complete once at most the later in-flight tiles'
+      // instructions are outstanding (loads complete in order)
+      const int later = min(n_wg - 1 - t, PREF - 1);
+      if (kvp && w == 0) wait_later<DMA_W + 1, PREF - 1>(later);
+      else wait_later<DMA_W, PREF - 1>(later);
+      __builtin_amdgcn_s_barrier();
+      if (t + PREF < n_wg) issue(t + PREF);
+      if (t >= n_vis) continue;
+      // per-tile read bases from an opaque lane id: otherwise the compiler
+      // precomputes every address of every stage outside the loop and spills
+      tile = (const char *)sm[t % NBUF];
+      int kbi[NKB];
+      lds_bases(kbi, vbi);
+      j0 = t * BN;
+      qk_tile(s, tile, kbi);
+      mask_and_max(s, mx, t, j0);
+      // first visible keys of a row: set the reference (nothing to rescale)
+      const bool init = (m_ref[0] == -INFINITY && mx[0] != -INFINITY) ||
+                        (m_ref[1] == -INFINITY && mx[1] != -INFINITY);
+      if (__builtin_amdgcn_ballot_w64(init) != 0) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          if (m_ref[rb] == -INFINITY) m_ref[rb] = max_xor32(mx[rb]);
+      }
+      const bool grow = (mx[0] > m_ref[0] + kRescale) || (mx[1] > m_ref[1] + kRescale);
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        need_rescale = true;
+        break;
+      }
+      pv_tile(s, tile, vbi);
+    }
+    if (!need_rescale) break;
+    // ---- cold path: move the reference max, rescale, finish tile t
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float m_new = fmaxf(m_ref[rb], max_xor32(mx[rb]));
+      const float alpha = (m_ref[rb] == -INFINITY) ? 0.f : exp2f(m_ref[rb] - m_new);
+      l_run[rb] *= alpha;
 #pragma unroll
       for (int b = 0; b < OB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[b][rb][i] *= alpha;
+      m_ref[rb] = m_new;
+    }
+    pv_tile(s, tile, vbi);
+    ++t;
+  }
+
+  // ---- epilogue: normalise; O^T -> LDS -> whole output rows
+  float inv[2], lse[2];
 #pragma unroll
-      for (int b = 0; b < OB; ++b) {
-        const __bf16 *vp = &sm.vt[(32 * b + n) * VP + 8 * hf];
+  for (int rb = 0; rb < 2; ++rb) {
+    const float l_tot = sum_xor32(l_run[rb]);
+    const bool any = l_tot > 0.f;
+    inv[rb] = any ? 1.f / l_tot : 0.f;
+    lse[rb] = any ? (m_ref[rb] + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();  // every wave is done with the tiles
+  constexpr int OSZ = 4;                       // bytes per staged element (fp32)
+  constexpr int OPITCH = DV * OSZ + 16;        // row pitch of the staging area
+  char *ost = (char *)sm + w * 32 * OPITCH;    // 32 rows per wave per pass
+  for (int rb = 0; rb < 2; ++rb) {
+    // this lane: row n of block rb, dv = 32*b + 8*(i/4) + 4*hf + (i%4)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 a = *(const bf16x8 *)(vp + 16 * ks);
-          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[b], 0, 0, 0);
+    for (int b = 0; b < OB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 x = make_float4(oacc[b][rb][4 * g] * inv[rb], oacc[b][rb][4 * g + 1] * inv[rb],
+                               oacc[b][rb][4 * g + 2] * inv[rb], oacc[b][rb][4 * g + 3] * inv[rb]);
+        *(float4 *)(ost + n * OPITCH + (32 * b + 8 * g + 4 * hf) * OSZ) = x;
+      }
+    if (hf == 0 && valid[rb]) {
+      const int64_t qrow = (int64_t)sd.q_begin + row0 + w * RW + rb * 32 + n;
+      p.lse[qrow * p.lse_rs + h] = lse[rb];
+    }
+    __builtin_amdgcn_s_barrier();  // (wave-local data; keeps the waves in step)
+    // whole rows: 8 output elements per lane
+    constexpr int LPR = DV / 8;                // lanes per row
+    constexpr int RPI = 64 / LPR;              // rows per instruction
+    const int sub = lane % LPR, rsub = lane / LPR;
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int r = r0 + rsub;
+      const int rr = w * RW + rb * 32 + r;
+      if (rr < rows_here) {
+        const float4 a = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ);
+        const float4 c = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ + 16);
+        const int64_t qrow = (int64_t)sd.q_begin + row0 + rr;
+        if (p.o_bf16) {
+          u32x4 v;
+          v[0] = pack_bf16(a.x, a.y);
+          v[1] = pack_bf16(a.z, a.w);
+          v[2] = pack_bf16(c.x, c.y);
+          v[3] = pack_bf16(c.z, c.w);
+          *(u32x4 *)((__bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + sub * 8) = v;
+        } else {
+          float *op = (float *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + sub * 8;
+          *(float4 *)op = a;
+          *(float4 *)(op + 4) = c;
         }
       }
     }
-    j0 = jn;
-    live = live_next;
-  }
-
-  // ---- epilogue: combine the two halves' sums, normalise, write
-  const float l_tot = l_run + xor32(l_run);
-  if (!valid) return;
-  const bool any = l_tot > 0.f;
-  const float inv = any ? 1.f / l_tot : 0.f;
-  if (hf == 0)
-    p.lse[qrow * p.lse_rs + h] = any ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  if (p.o_bf16) {
-    __bf16 *op = (__bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + 4 * hf;
-#pragma unroll
-    for (int b = 0; b < OB; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 x;
-        x[0] = pack_bf16(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-        x[1] = pack_bf16(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-        *(u32x2 *)(op + 32 * b + 8 * g) = x;
-      }
-  } else {
-    float *op = (float *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + 4 * hf;
-#pragma unroll
-    for (int b = 0; b < OB; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4 x = make_float4(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv,
-                               oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-        *(float4 *)(op + 32 * b + 8 * g) = x;
-      }
+    __builtin_amdgcn_s_barrier();
   }
 }
 

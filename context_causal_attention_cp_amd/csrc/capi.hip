@@ -46,7 +46,7 @@ cp_status check_attn(const cp_attn_args *a) {
   if (a->num_q_rows < 0 || a->num_kv_rows < 0 || a->num_segs < 0) return CP_ERR_ARG;
   if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv != 0) return CP_ERR_ARG;
   if (a->dqk < 1 || a->dv < 1) return CP_ERR_ARG;
-  if (!std::isfinite(a->scale)) return CP_ERR_ARG;
+  if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return CP_ERR_ARG;
   if (a->num_segs > 0 && !a->segs) return CP_ERR_ARG;
   for (int32_t i = 0; i < a->num_segs; ++i) {
     const cp_segment &s = a->segs[i];
@@ -62,6 +62,11 @@ cp_status check_attn(const cp_attn_args *a) {
   }
   const Path path = pick_path(*a);
   if (path == Path::None) return CP_ERR_UNSUPPORTED;
+  if (path == Path::Bf16Mfma) {
+    // a K or V tile (up to 64 rows) is addressed with 32-bit byte offsets
+    const int64_t rs = std::max(a->k_row_stride, a->v_row_stride);
+    if (64 * rs * 2 > INT32_MAX) return CP_ERR_UNSUPPORTED;
+  }
   if (path == Path::DecodeMla) {
     // the latent rows of a segment are addressed with 32-bit byte offsets
     for (int32_t i = 0; i < a->num_segs; ++i) {
