@@ -41,10 +41,11 @@ namespace cpattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NW = 4;          // waves
 constexpr int NT = 64 * NW;    // threads
@@ -77,10 +78,9 @@ __device__ inline int find_seg(const LaunchSegs &L, int tile_order) {
   return si;
 }
 
+// two floats -> two bf16 (round to nearest even) in one instruction
 __device__ inline uint32_t pack_bf16(float a, float b) {
-  const __bf16 lo = (__bf16)a, hi = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 __device__ inline float max_xor32(float x) {
@@ -126,49 +126,34 @@ __device__ inline void wait_later(int later) {
   wait_vm<0>();
 }
 
-// XOR swizzles of the 16-byte chunk index inside a tile row (key bits k0..k3).
-//  K rows are read as 16 consecutive keys at one chunk: with 8 mod 16 chunks
-//  per row the swizzle is (k0^k3) | (k0^k1)<<1 | (k0^k2)<<2 (inside aligned
-//  groups of 8 chunks); with 16 chunks per row it is the key's low 4 bits.
-//  V rows are read transposed, 4 consecutive keys x 4 chunks: key bits 0,1 go
-//  to chunk bits 1,2 (and 3).  Both keep those reads free of bank conflicts
-//  for 32- and 64-bank LDS.
-template <int KCH>
-__device__ inline int kswz(int key) {
-  if constexpr (KCH % 16 == 0) {
-    return key & 15;
-  } else {
-    const int k0 = key & 1, k1 = (key >> 1) & 1, k2 = (key >> 2) & 1, k3 = (key >> 3) & 1;
-    return (k0 ^ k3) | ((k0 ^ k1) << 1) | ((k0 ^ k2) << 2);
-  }
-}
-template <int VCH>
-__device__ inline int vswz(int key) {
-  const int k0 = key & 1, k1 = (key >> 1) & 1;
-  if constexpr (VCH % 16 == 0) return (k0 << 1) | (k1 << 2) | (k0 << 3);
-  else return (k0 << 1) | (k1 << 2);
-}
-
-// Tile width and LDS stages per head-dim pair: 64-key tiles and 3 stages
-// where registers allow; 32-key tiles and 6 stages (five tiles prefetched)
-// for the 192-wide K, whose Q fragments need 96 registers.
+// LDS layouts of one stage (16-byte units; keys fastest, so no swizzle):
+//   K  unit ((key/16)*KCH + chunk)*16 + key%16   -- a K fragment read (32 keys
+//      of one chunk) is 2 x 256 contiguous bytes;
+//   V  unit ((key/4)*VCH + chunk)*4 + key%4      -- a transposing read (4 keys
+//      x 16 columns per 16 lanes) is 128 contiguous bytes;
+//   then BN key positions (4 bytes each).
+// One DMA instruction fills 64 consecutive units, so every lane's global
+// offset is a per-lane constant plus a per-instruction uniform term.
 template <int DQK, int DV>
 struct Cfg {
-  static constexpr int BN = DQK > 128 ? 32 : 64;   // keys per tile
-  static constexpr int NBUF = DQK > 128 ? 6 : 3;   // LDS stages
-  static constexpr int NKB_ = BN / 32;             // 32-key blocks per tile
-  static constexpr int KSTEP = BN / 16;            // 16-key PV steps per tile
-  static constexpr int KCH = DQK / 8;          // 16-byte chunks per K row
-  static constexpr int VCH = DV / 8;           // ... per V row
-  static constexpr int KTILE = BN * KCH;       // chunks per K tile
-  static constexpr int KPOS = BN * (KCH + VCH);  // key positions after K and V
-  static constexpr int STAGE = KPOS + BN / 4;
-  static constexpr int KDMA = BN * KCH / 64 / NW;  // K DMA instructions per wave per stage
-  static constexpr int VDMA = BN * VCH / 64 / NW;
-  static constexpr int KS = DQK / 16;          // QK k-steps
-  static constexpr int OB = DV / 32;           // 32-row dv blocks
-  static_assert((BN * KCH / 64) % NW == 0 && (BN * VCH / 64) % NW == 0, "DMA split");
-  static_assert(KCH % 8 == 0 && VCH % 8 == 0, "swizzle groups");
+  static constexpr int BN = 32;                    // keys per tile
+  static constexpr int KCH = DQK / 8;              // 16-byte chunks per K row
+  static constexpr int VCH = DV / 8;               // ... per V row
+  static constexpr int KUNITS = BN * KCH;
+  static constexpr int VUNITS = BN * VCH;
+  static constexpr int KPOS = KUNITS + VUNITS;     // key positions
+  static constexpr int STAGE = KPOS + BN / 4;      // units per stage
+  static constexpr int NBUF_FIT = 160 * 1024 / (STAGE * 16);
+  static constexpr int NBUF = NBUF_FIT < 8 ? NBUF_FIT : 8;  // LDS stages
+  // tiles in flight beyond the two being read (K of tile t+1, V of tile t)
+  static constexpr int PREF = NBUF - 2;
+  static constexpr int KDMA = KUNITS / 64 / NW;    // DMA instructions per wave per stage
+  static constexpr int VDMA = VUNITS / 64 / NW;
+  static constexpr int KS = DQK / 16;              // QK k-steps
+  static constexpr int OB = DV / 32;               // 32-row dv blocks
+  static_assert(KUNITS % (64 * NW) == 0 && VUNITS % (64 * NW) == 0, "DMA split");
+  static_assert(KCH % 4 == 0 && (VCH == 8 || VCH == 16), "layout");
+  static_assert(NBUF >= 3 && PREF * (KDMA + VDMA + 1) < 64, "stages");
 };
 
 template <int DQK, int DV>
@@ -176,7 +161,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   using C = Cfg<DQK, DV>;
   constexpr int KCH = C::KCH, VCH = C::VCH, KS = C::KS, OB = C::OB;
-  constexpr int BN = C::BN, NBUF = C::NBUF, NKBLK = C::NKB_, KSTEP = C::KSTEP;
+  constexpr int BN = C::BN, NBUF = C::NBUF, PREF = C::PREF;
   __shared__ __attribute__((aligned(1024))) u32x4 sm[C::NBUF][C::STAGE];
 
   const int tid = threadIdx.x;
@@ -254,69 +239,67 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     }
   }
 
-  // ---- LDS DMA of one stage: K rows then V rows of keys [j0, j0 + 64)
+  // ---- LDS DMA of one stage (K units, V units, key positions of a tile).
+  // K instruction I: keys 16*(4I/KCH) + lane%16, chunk (4I)%KCH + lane/16.
+  // V instruction I: keys 4*(16I/VCH + (lane/4)/VCH) + lane%4, chunk (lane/4)%VCH.
   const __bf16 *kbase = (const __bf16 *)p.k + (int64_t)sd.kv_begin * p.k_rs + (int64_t)kvh * p.k_hs;
   const __bf16 *vbase = (const __bf16 *)p.v + (int64_t)sd.kv_begin * p.v_rs + (int64_t)kvh * p.v_hs;
+  const uint32_t k_rb = (uint32_t)p.k_rs * 2u, v_rb = (uint32_t)p.v_rs * 2u;  // row bytes
+  const uint32_t k_lane = (uint32_t)(lane & 15) * k_rb + (uint32_t)(lane >> 4) * 16u;
+  const uint32_t v_lane =
+      (uint32_t)(4 * ((lane >> 2) / VCH) + (lane & 3)) * v_rb + (uint32_t)((lane >> 2) % VCH) * 16u;
   auto issue = [&](int t) {
     const int j0 = t * BN;
     const int nrows = min(BN, n_kv - j0);
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(kbase + (int64_t)j0 * p.k_rs), (short)0, (int)(nrows * p.k_rs * 2), 0x00020000);
+        (void *)(kbase + (int64_t)j0 * p.k_rs), (short)0, (int)(nrows * k_rb), 0x00020000);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(vbase + (int64_t)j0 * p.v_rs), (short)0, (int)(nrows * p.v_rs * 2), 0x00020000);
+        (void *)(vbase + (int64_t)j0 * p.v_rs), (short)0, (int)(nrows * v_rb), 0x00020000);
     u32x4 *dst = sm[t % NBUF];
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // recomputed per stage, not kept live
 #pragma unroll
     for (int i = 0; i < C::KDMA; ++i) {
-      const int slot = (w * C::KDMA + i) * 64 + ln;
-      const int key = slot / KCH, cs = slot % KCH;
-      const uint32_t off = (uint32_t)(key * p.k_rs + (cs ^ kswz<KCH>(key)) * 8) * 2u;
+      const int I = w * C::KDMA + i;
+      const uint32_t off = k_lane + (uint32_t)(16 * (4 * I / KCH)) * k_rb + (uint32_t)((4 * I) % KCH) * 16u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          kr, (__attribute__((address_space(3))) void *)(dst + (w * C::KDMA + i) * 64), 16, off,
-          0, 0, 0);
+          kr, (__attribute__((address_space(3))) void *)(dst + I * 64), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::VDMA; ++i) {
-      const int slot = (w * C::VDMA + i) * 64 + ln;
-      const int key = slot / VCH, cs = slot % VCH;
-      const uint32_t off = (uint32_t)(key * p.v_rs + (cs ^ vswz<VCH>(key)) * 8) * 2u;
+      const int I = w * C::VDMA + i;
+      const uint32_t off = v_lane + (uint32_t)(4 * (16 * I / VCH)) * v_rb;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vr, (__attribute__((address_space(3))) void *)(dst + C::KTILE + (w * C::VDMA + i) * 64),
-          16, off, 0, 0, 0);
+          vr, (__attribute__((address_space(3))) void *)(dst + C::KUNITS + I * 64), 16, off, 0,
+          0, 0);
     }
-    if (kvp && w == 0 && ln < BN) {
+    if (kvp && w == 0 && lane < BN) {
       const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(kvp + j0), (short)0, nrows * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          pr, (__attribute__((address_space(3))) void *)(dst + C::KPOS), 4, (uint32_t)ln * 4u, 0,
-          0, 0);
+          pr, (__attribute__((address_space(3))) void *)(dst + C::KPOS), 4, (uint32_t)lane * 4u,
+          0, 0, 0);
     }
+  };
+  constexpr int DMA_W = C::KDMA + C::VDMA;
+  // tile u's DMA is complete once at most the later in-flight tiles'
+  // instructions are outstanding (loads complete in order); then every wave
+  // has it after the barrier
+  auto wait_tile = [&](int u) {
+    const int later = min(n_wg - 1 - u, PREF - 1);
+    if (kvp && w == 0) wait_later<DMA_W + 1, PREF - 1>(later);
+    else wait_later<DMA_W, PREF - 1>(later);
+    __builtin_amdgcn_s_barrier();
+    if (u + PREF < n_wg) issue(u + PREF);
   };
 
-  // per-lane LDS byte offsets: K row reads (key 32*nb + n, chunk 2*s + hf =
-  // 8*(s>>2) + (2*(s&3) + hf)), V transposing reads (key 16*ks + 4*hf + li/4
-  // (+8), dv 32*mb + 16*(blk&1) + 4*(li&3)).  They are rebuilt every tile
-  // from an opaque copy of the lane id (a few integer ops) rather than kept
-  // live across the loop.
-  constexpr int kKeyBytes = KCH * 16;
-  // 3-bit swizzle: chunk 2*s + hf = 8*(s>>2) + (2*(s&3) + hf) -> 4 bases + an
-  // immediate; 4-bit swizzle (16-chunk rows): one base per k-step
-  constexpr bool kSw4 = (KCH % 16 == 0);
-  constexpr int NKB = kSw4 ? KS : 4;
-  auto lds_bases = [&](int (&kbo)[NKB], int (&vbo)[OB]) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int nn = ln & 31, hh = ln >> 5, lli = ln & 15, bb = ln >> 4;
-#pragma unroll
-    for (int s4 = 0; s4 < NKB; ++s4) kbo[s4] = 16 * (nn * KCH + ((2 * s4 + hh) ^ kswz<KCH>(nn)));
-    const int vkey = 4 * hh + (lli >> 2);
-#pragma unroll
-    for (int mb = 0; mb < OB; ++mb) {
-      const int chunk = 4 * mb + 2 * (bb & 1) + ((lli & 3) >> 1);
-      vbo[mb] = C::KTILE * 16 + 16 * (vkey * VCH + (chunk ^ vswz<VCH>(vkey))) + 8 * (lli & 1);
-    }
-  };
+  // per-lane LDS byte offsets inside a stage
+  //  K fragment (A of S^T): key n, chunk 2*s + hf   -> kq + 512*s
+  //  V^T fragment (A of O^T, transposing read): 16-lane block bb, lane li
+  //  addresses key 16*ks + 4*hf + 8*hi + li/4, dv 32*mb + 16*(bb&1) + 4*(li&3)
+  //                                                  -> vt + 64*(4*VCH*ks + 2*VCH*hi + 4*mb)
+  const int li = lane & 15, bb = lane >> 4;
+  const int kq = ((n >> 4) * KCH + hf) * 256 + (n & 15) * 16;
+  const int vt = C::KUNITS * 16 +
+                 ((hf * VCH + 2 * (bb & 1) + ((li & 3) >> 1)) * 4 + (li >> 2)) * 16 + 8 * (li & 1);
 
   f32x16 oacc[OB][2];
 #pragma unroll
@@ -329,152 +312,110 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   float l_run[2] = {0.f, 0.f};              // this half's partial row sums
   const float sl2 = p.scale_log2;
 
-  // S^T = K Q^T for one tile: 2 key blocks x 2 row blocks
-  auto qk_tile = [&](f32x16 (&sc)[NKBLK][2], const char *tl, const int (&kbi)[NKB]) {
+  // S^T = K Q^T of one tile (32 keys x 2 row blocks)
+  auto qk = [&](f32x16 (&sc)[2], const char *tl) {
 #pragma unroll
-    for (int nb = 0; nb < NKBLK; ++nb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int i = 0; i < 16; ++i) sc[rb][i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[nb][rb][i] = 0.f;
+    for (int st = 0; st < KS; ++st) {
+      const bf16x8 a = *(const bf16x8 *)(tl + kq + 512 * st);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][st], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][st], sc[1], 0, 0, 0);
+    }
+  };
+  // boundary tiles: keys past the segment or after the row's position
+  auto mask = [&](f32x16 (&sc)[2], const char *tl, int j0) {
+    const int *kp = (const int *)(tl + C::KPOS * 16);
 #pragma unroll
-    for (int nb = 0; nb < NKBLK; ++nb) {
+    for (int i = 0; i < 16; ++i) {
+      const int kj = 8 * (i >> 2) + 4 * hf + (i & 3);
+      const int kpos = kvp ? kp[kj] : j0 + kj;
+      const bool in = j0 + kj < n_kv;
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const int koff = kSw4 ? kbi[st] : kbi[st & 3] + 128 * (st >> 2);
-        const bf16x8 a = *(const bf16x8 *)(tl + koff + 32 * nb * kKeyBytes);
-        sc[nb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][st], sc[nb][0], 0, 0, 0);
-        sc[nb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][st], sc[nb][1], 0, 0, 0);
+      for (int rb = 0; rb < 2; ++rb) {
+        const bool vis = in && (!p.causal || kpos <= qpos[rb]);
+        sc[rb][i] = vis ? sc[rb][i] : -INFINITY;
       }
     }
   };
-  // mask on boundary tiles; lane-local row max (log2 units) per row block
-  auto mask_and_max = [&](f32x16 (&sc)[NKBLK][2], float (&m2)[2], int tt, int jj0) {
-    if (tt >= n_full) {
-      const int *kp = (const int *)(sm[tt % NBUF] + C::KPOS);
-#pragma unroll
-      for (int nb = 0; nb < NKBLK; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kj = 32 * nb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const int kpos = kvp ? kp[kj] : jj0 + kj;
-          const bool in = jj0 + kj < n_kv;
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            const bool vis = in && (!p.causal || kpos <= qpos[rb]);
-            sc[nb][rb][i] = vis ? sc[nb][rb][i] : -INFINITY;
-          }
-        }
-    }
+  // lane-local row max in log2 units
+  auto rowmax = [&](const f32x16 (&sc)[2], float (&m2)[2]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float m = -INFINITY;
 #pragma unroll
-      for (int nb = 0; nb < NKBLK; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[nb][rb][i]);
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[rb][i]);
       m2[rb] = m * sl2;
     }
   };
-  // per 16-key step: P = exp2(s*scale*log2e - m) packed as the B operand,
-  // then O^T += V^T P^T with V^T from transposing reads shared by both row
-  // blocks (P is made just before use to keep few registers live)
-  auto pv_tile = [&](f32x16 (&sc)[NKBLK][2], const char *tl, const int (&vbi)[OB]) {
-    float mneg[2], ls[2] = {0.f, 0.f};
+  // P of 16-key step c: exp2(s*scale*log2e - m_ref) as the B operand
+  // (element e <-> key 16c + 8*(e/4) + 4*hf + e%4); row sums in fp32 (the
+  // log-sum-exp keeps fp32 accuracy)
+  auto probs = [&](const f32x16 (&sc)[2], int c, bf16x8 (&pf)[2], float (&ls)[2]) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) mneg[rb] = (m_ref[rb] == -INFINITY) ? 0.f : -m_ref[rb];
+    for (int rb = 0; rb < 2; ++rb) {
+      const float mneg = (m_ref[rb] == -INFINITY) ? 0.f : -m_ref[rb];
+      u32x4 pk;
 #pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) {
-      const int nb = ks >> 1, c = ks & 1;
-      // V^T fragments of this step (transposing reads), shared by both row
-      // blocks; issued first so the exponentials below hide their latency
-      u32x2 vl[OB], vh[OB];
-#pragma unroll
-      for (int b = 0; b < OB; ++b) {
-        const char *vp = tl + vbi[b] + 16 * ks * VCH * 16;
-        vl[b] = lds_read_tr16(vp);
-        vh[b] = lds_read_tr16(vp + 8 * VCH * 16);
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * c + 2 * e], sl2, mneg));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * c + 2 * e + 1], sl2, mneg));
+        ls[rb] += p0 + p1;
+        pk[e] = pack_bf16(p0, p1);
       }
-      bf16x8 pf[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[nb][rb][8 * c + 2 * e], sl2, mneg[rb]));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[nb][rb][8 * c + 2 * e + 1], sl2, mneg[rb]));
-          ls[rb] += p0 + p1;
-          pk[e] = pack_bf16(p0, p1);
-        }
-        pf[rb] = __builtin_bit_cast(bf16x8, pk);
-      }
-#pragma unroll
-      for (int b = 0; b < OB; ++b) lds_wait(vl[b], vh[b]);
-#pragma unroll
-      for (int b = 0; b < OB; ++b) {
-        const u32x4 av = {vl[b][0], vl[b][1], vh[b][0], vh[b][1]};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-        oacc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0], oacc[b][0], 0, 0, 0);
-        oacc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1], oacc[b][1], 0, 0, 0);
-      }
+      pf[rb] = __builtin_bit_cast(bf16x8, pk);
     }
+  };
+  // O^T += V^T P^T for 16-key step c of the tile at tl
+  auto pv = [&](const char *tl, int c, const bf16x8 (&pf)[2]) {
+    u32x2 vl[OB], vh[OB];
+#pragma unroll
+    for (int b = 0; b < OB; ++b) {
+      const char *vp = tl + vt + 64 * (4 * VCH * c + 4 * b);
+      vl[b] = lds_read_tr16(vp);
+      vh[b] = lds_read_tr16(vp + 64 * 2 * VCH);
+    }
+#pragma unroll
+    for (int b = 0; b < OB; ++b) lds_wait(vl[b], vh[b]);
+#pragma unroll
+    for (int b = 0; b < OB; ++b) {
+      const u32x4 av = {vl[b][0], vl[b][1], vh[b][0], vh[b][1]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+      oacc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0], oacc[b][0], 0, 0, 0);
+      oacc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1], oacc[b][1], 0, 0, 0);
+    }
+  };
+  auto stage = [&](int t) { return (const char *)sm[t % NBUF]; };
+  float mx[2];
+  auto grows = [&]() {
+    return __builtin_amdgcn_ballot_w64((mx[0] > m_ref[0] + kRescale) ||
+                                       (mx[1] > m_ref[1] + kRescale)) != 0;
+  };
+  // One pipelined step: S of tile t + 1 and the first half of PV of tile t on
+  // the matrix cores while the exponentials of tile t run; then the second
+  // half of PV while the max of tile t + 1 is taken.  Returns whether a row
+  // of tile t + 1 outgrew its reference.
+  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int t) -> bool {
+    const int u = t + 1;
+    wait_tile(u);
+    const char *tc = stage(t), *tn = stage(u);
+    float ls[2] = {0.f, 0.f};
+    bf16x8 pf0[2], pf1[2];
+    qk(nxt, tn);
+    probs(cur, 0, pf0, ls);
+    pv(tc, 0, pf0);
+    probs(cur, 1, pf1, ls);
+    if (u >= n_full) mask(nxt, tn, u * BN);
+    rowmax(nxt, mx);
+    pv(tc, 1, pf1);
     l_run[0] += ls[0];
     l_run[1] += ls[1];
+    return grows();
   };
-
-  constexpr int PREF = NBUF - 1;  // tiles in flight ahead of the one computed
-#pragma unroll
-  for (int i = 0; i < PREF; ++i)
-    if (i < n_wg) issue(i);
-  constexpr int DMA_W = C::KDMA + C::VDMA;
-
-  // The tile loop.  The hot path never rescales the accumulator: the first
-  // visible tile of a row only sets its reference max (O and l are still
-  // zero), and a later growth beyond the headroom leaves the loop for the
-  // cold path below, which rescales and then finishes that tile.
-  int t = 0;
-  f32x16 s[NKBLK][2];
-  float mx[2];
-  const char *tile = nullptr;
-  int j0 = 0;
-  int vbi[OB];
-  while (true) {
-    bool need_rescale = false;
-    for (; t < n_wg; ++t) {
-      t = __builtin_amdgcn_readfirstlane(t);  // uniform loop counter
-      // tile t's DMA is complete once at most the later in-flight tiles'
-      // instructions are outstanding (loads complete in order)
-      const int later = min(n_wg - 1 - t, PREF - 1);
-      if (kvp && w == 0) wait_later<DMA_W + 1, PREF - 1>(later);
-      else wait_later<DMA_W, PREF - 1>(later);
-      __builtin_amdgcn_s_barrier();
-      if (t + PREF < n_wg) issue(t + PREF);
-      if (t >= n_vis) continue;
-      // per-tile read bases from an opaque lane id: otherwise the compiler
-      // precomputes every address of every stage outside the loop and spills
-      tile = (const char *)sm[t % NBUF];
-      int kbi[NKB];
-      lds_bases(kbi, vbi);
-      j0 = t * BN;
-      qk_tile(s, tile, kbi);
-      mask_and_max(s, mx, t, j0);
-      // first visible keys of a row: set the reference (nothing to rescale)
-      const bool init = (m_ref[0] == -INFINITY && mx[0] != -INFINITY) ||
-                        (m_ref[1] == -INFINITY && mx[1] != -INFINITY);
-      if (__builtin_amdgcn_ballot_w64(init) != 0) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          if (m_ref[rb] == -INFINITY) m_ref[rb] = max_xor32(mx[rb]);
-      }
-      const bool grow = (mx[0] > m_ref[0] + kRescale) || (mx[1] > m_ref[1] + kRescale);
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        need_rescale = true;
-        break;
-      }
-      pv_tile(s, tile, vbi);
-    }
-    if (!need_rescale) break;
-    // ---- cold path: move the reference max, rescale, finish tile t
+  // move the reference max (rare): O and l of the rows scale by exp2(old - new)
+  auto rescale = [&]() {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const float m_new = fmaxf(m_ref[rb], max_xor32(mx[rb]));
@@ -486,9 +427,51 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
         for (int i = 0; i < 16; ++i) oacc[b][rb][i] *= alpha;
       m_ref[rb] = m_new;
     }
-    pv_tile(s, tile, vbi);
+  };
+
+#pragma unroll
+  for (int i = 0; i < PREF; ++i)
+    if (i < n_wg) issue(i);
+
+  f32x16 sa[2], sb[2];
+  int t = 0;  // the tile whose scores are in sa
+  if (n_vis > 0) {
+    wait_tile(0);
+    qk(sa, stage(0));
+    if (n_full == 0) mask(sa, stage(0), 0);
+    rowmax(sa, mx);
+    // first keys: O and l are still zero, only the reference is set
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) m_ref[rb] = max_xor32(mx[rb]);
+    // The hot loop runs two steps per trip so the score buffers alternate
+    // without copies; a reference move (rare) rescales O and l in place.
+    while (t + 2 < n_vis) {
+      if (step(sa, sb, t)) rescale();
+      if (step(sb, sa, t + 1)) rescale();
+      t += 2;
+    }
+    if (t + 1 < n_vis) {
+      if (step(sa, sb, t)) rescale();
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sa[rb] = sb[rb];
+      t += 1;
+    }
+    // the last visible tile: exponentials and PV only
+    {
+      float ls[2] = {0.f, 0.f};
+      bf16x8 pf0[2], pf1[2];
+      const char *tc = stage(t);
+      probs(sa, 0, pf0, ls);
+      pv(tc, 0, pf0);
+      probs(sa, 1, pf1, ls);
+      pv(tc, 1, pf1);
+      l_run[0] += ls[0];
+      l_run[1] += ls[1];
+    }
     ++t;
   }
+  // tiles other waves still compute: keep the barriers and the DMA in step
+  for (; t < n_wg; ++t) wait_tile(t);
 
   // ---- epilogue: normalise; O^T -> LDS -> whole output rows
   float inv[2], lse[2];
@@ -502,6 +485,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   __syncthreads();  // every wave is done with the tiles
   constexpr int OSZ = 4;                       // bytes per staged element (fp32)
   constexpr int OPITCH = DV * OSZ + 16;        // row pitch of the staging area
+  static_assert(NW * 32 * OPITCH <= NBUF * C::STAGE * 16, "staging fits the stages");
   char *ost = (char *)sm + w * 32 * OPITCH;    // 32 rows per wave per pass
   for (int rb = 0; rb < 2; ++rb) {
     // this lane: row n of block rb, dv = 32*b + 8*(i/4) + 4*hf + (i%4)
