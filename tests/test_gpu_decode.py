@@ -128,3 +128,26 @@ def test_decode_mla_b64_workload():
         err = float((l - np.log(w.ctx_len // W)).abs().max())
         say(f"  q=0 closed form shard {j}: max|dLSE|={err:.2e}")
         assert err < 1e-3
+
+
+@pytest.mark.parametrize("val", [0.05, 0.25])
+def test_decode_reference_growth(val):
+    """One key far above every other score, after the first tile: 0.05 lifts
+    the row max by about 2^41 (log2 units) over the first tile's, 0.25 by
+    about 2^207 (beyond the fp32 range of exp without a moved reference).
+    The kernel's softmax reference handling must still give the plain
+    definition's result."""
+    B, ctx, hq = 2, 3000, 128
+    q = torch.ones((B, hq, DQK), device=DEV, dtype=torch.bfloat16)
+    kv = torch.zeros((B, ctx, DQK), device=DEV, dtype=torch.bfloat16)
+    kv[0, 2000] = val
+    kv[1, 37] = val
+    kv[1, 2999] = -val
+    say(f"decode reference growth val={val}")
+    outs = _run_shards(q, kv, 1, 1.0)
+    torch.cuda.synchronize()
+    q64, kv64 = f64(q), f64(kv)
+    o, l = outs[0]
+    for b in range(B):
+        ro, rl = _oracle_shard(q64, kv64, b, 0, 1, 1.0, ctx)
+        compare(f64(o[b]), f64(l[b]), ro, rl, range(hq), "bf16", f"req {b}")
