@@ -199,12 +199,12 @@ def main():
             "avg_launch_ms": round(attn_launch_ms, 4),
         },
         "merge": {
-            "kernel": "lse_merge_kernel<bf16,bf16>",
+            "kernel": "lse_merge_kernel<16,bf16,bf16>",
             "ms": round(merge_ms_avg, 4),
             "algorithmic_bytes": merge_bytes,
             "GB/s": round(merge_gbs, 1),
             "frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4),
-            "traffic": _profiled_traffic("lse_merge_kernel<bf16,bf16>", "lse_merge.hip"),
+            "traffic": _profiled_traffic("lse_merge_kernel<16,bf16,bf16>", "lse_merge.hip"),
         },
     }
     del kv, o_parts, l_parts
@@ -311,6 +311,7 @@ def _decode(cp, w):
     return {"shard_ms": round(ms, 4), "algorithmic_bytes_per_shard": by,
             "GB/s": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
             "TFLOP/s": round(fl / ms / 1e9, 1), "workspace_bytes": int(ws.numel()),
+            "traffic": _profiled_traffic("attn_decode_mla_kernel", "attn_decode_mla.hip"),
             "merge_ms": round(mms, 4), "merge_GB/s": round(mby / mms / 1e6, 1),
             "merge_frac_hbm": round(mby / mms / 1e6 / PEAK_HBM_GBS, 4),
             "merge_note": "the partials (134 MB) fit the 256 MB Infinity Cache: effective rate"}
