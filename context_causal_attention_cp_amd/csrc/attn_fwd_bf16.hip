@@ -49,8 +49,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NW = 4;          // waves
 constexpr int NT = 64 * NW;    // threads
-constexpr int RW = 64;         // query rows per wave
-constexpr int BM = RW * NW;    // query rows per workgroup
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescale = 8.0f;
 constexpr int kNoPos = -(1 << 30);
@@ -156,10 +154,14 @@ struct Cfg {
   static_assert(NBUF >= 3 && PREF * (KDMA + VDMA + 1) < 64, "stages");
 };
 
-template <int DQK, int DV>
+// RB = 32-row MFMA column blocks per wave: 2 (256-row workgroups) or 1
+// (128-row workgroups, for launches too small to fill the chip otherwise)
+template <int DQK, int DV, int RB>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   using C = Cfg<DQK, DV>;
+  constexpr int RW = 32 * RB;    // query rows per wave
+  constexpr int BM = RW * NW;    // query rows per workgroup
   constexpr int KCH = C::KCH, VCH = C::VCH, KS = C::KS, OB = C::OB;
   constexpr int BN = C::BN, NBUF = C::NBUF, PREF = C::PREF;
   __shared__ __attribute__((aligned(1024))) u32x4 sm[C::NBUF][C::STAGE];
@@ -180,11 +182,11 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   const int rows_here = min(BM, sd.q_len - row0);
   const int kvh = h / (p.hq / p.hkv);
 
-  // ---- this lane's two query rows (row blocks rb = 0, 1)
-  int qpos[2];
-  bool valid[2];
+  // ---- this lane's query rows (one per row block)
+  int qpos[RB];
+  bool valid[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int rr = w * RW + rb * 32 + n;
     valid[rb] = rr < rows_here;
     qpos[rb] = valid[rb] ? sd.pos_begin + (row0 + rr) * sd.pos_stride : kNoPos;
@@ -226,9 +228,9 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   if (nvalid_w == 0) n_vis = n_full = 0;
 
   // ---- Q fragments: B operand of S^T = K Q^T (n = row, k = d)
-  bf16x8 qf[2][KS];
+  bf16x8 qf[RB][KS];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int64_t qrow = (int64_t)sd.q_begin + row0 + w * RW + rb * 32 + n;
     const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)h * p.q_hs + 8 * hf;
 #pragma unroll
@@ -301,32 +303,37 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   const int vt = C::KUNITS * 16 +
                  ((hf * VCH + 2 * (bb & 1) + ((li & 3) >> 1)) * 4 + (li >> 2)) * 16 + 8 * (li & 1);
 
-  f32x16 oacc[OB][2];
+  f32x16 oacc[OB][RB];
 #pragma unroll
   for (int b = 0; b < OB; ++b)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[b][rb][i] = 0.f;
-  float m_ref[2] = {-INFINITY, -INFINITY};  // reference max (log2 units) per row block
-  float l_run[2] = {0.f, 0.f};              // this half's partial row sums
+  float m_ref[RB], l_run[RB];  // reference max (log2 units), this half's row sums
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
   const float sl2 = p.scale_log2;
 
-  // S^T = K Q^T of one tile (32 keys x 2 row blocks)
-  auto qk = [&](f32x16 (&sc)[2], const char *tl) {
+  // S^T = K Q^T of one tile (32 keys x RB row blocks)
+  auto qk = [&](f32x16 (&sc)[RB], const char *tl) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[rb][i] = 0.f;
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
       const bf16x8 a = *(const bf16x8 *)(tl + kq + 512 * st);
-      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][st], sc[0], 0, 0, 0);
-      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][st], sc[1], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][st], sc[rb], 0, 0, 0);
     }
   };
   // boundary tiles: keys past the segment or after the row's position
-  auto mask = [&](f32x16 (&sc)[2], const char *tl, int j0) {
+  auto mask = [&](f32x16 (&sc)[RB], const char *tl, int j0) {
     const int *kp = (const int *)(tl + C::KPOS * 16);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -334,16 +341,16 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
       const int kpos = kvp ? kp[kj] : j0 + kj;
       const bool in = j0 + kj < n_kv;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         const bool vis = in && (!p.causal || kpos <= qpos[rb]);
         sc[rb][i] = vis ? sc[rb][i] : -INFINITY;
       }
     }
   };
   // lane-local row max in log2 units
-  auto rowmax = [&](const f32x16 (&sc)[2], float (&m2)[2]) {
+  auto rowmax = [&](const f32x16 (&sc)[RB], float (&m2)[RB]) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[rb][i]);
@@ -353,9 +360,9 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   // P of 16-key step c: exp2(s*scale*log2e - m_ref) as the B operand
   // (element e <-> key 16c + 8*(e/4) + 4*hf + e%4); row sums in fp32 (the
   // log-sum-exp keeps fp32 accuracy)
-  auto probs = [&](const f32x16 (&sc)[2], int c, bf16x8 (&pf)[2], float (&ls)[2]) {
+  auto probs = [&](const f32x16 (&sc)[RB], int c, bf16x8 (&pf)[RB], float (&ls)[RB]) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       const float mneg = (m_ref[rb] == -INFINITY) ? 0.f : -m_ref[rb];
       u32x4 pk;
 #pragma unroll
@@ -369,7 +376,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     }
   };
   // O^T += V^T P^T for 16-key step c of the tile at tl
-  auto pv = [&](const char *tl, int c, const bf16x8 (&pf)[2]) {
+  auto pv = [&](const char *tl, int c, const bf16x8 (&pf)[RB]) {
     u32x2 vl[OB], vh[OB];
 #pragma unroll
     for (int b = 0; b < OB; ++b) {
@@ -383,26 +390,33 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     for (int b = 0; b < OB; ++b) {
       const u32x4 av = {vl[b][0], vl[b][1], vh[b][0], vh[b][1]};
       const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-      oacc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0], oacc[b][0], 0, 0, 0);
-      oacc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1], oacc[b][1], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        oacc[b][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb], oacc[b][rb], 0, 0, 0);
     }
   };
   auto stage = [&](int t) { return (const char *)sm[t % NBUF]; };
-  float mx[2];
+  float mx[RB];
   auto grows = [&]() {
-    return __builtin_amdgcn_ballot_w64((mx[0] > m_ref[0] + kRescale) ||
-                                       (mx[1] > m_ref[1] + kRescale)) != 0;
+    bool g = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) g = g || (mx[rb] > m_ref[rb] + kRescale);
+    return __builtin_amdgcn_ballot_w64(g) != 0;
+  };
+  auto add_ls = [&](const float (&ls)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_run[rb] += ls[rb];
   };
   // One pipelined step: S of tile t + 1 and the first half of PV of tile t on
   // the matrix cores while the exponentials of tile t run; then the second
   // half of PV while the max of tile t + 1 is taken.  Returns whether a row
   // of tile t + 1 outgrew its reference.
-  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int t) -> bool {
+  auto step = [&](f32x16 (&cur)[RB], f32x16 (&nxt)[RB], int t) -> bool {
     const int u = t + 1;
     wait_tile(u);
     const char *tc = stage(t), *tn = stage(u);
-    float ls[2] = {0.f, 0.f};
-    bf16x8 pf0[2], pf1[2];
+    float ls[RB] = {};
+    bf16x8 pf0[RB], pf1[RB];
     qk(nxt, tn);
     probs(cur, 0, pf0, ls);
     pv(tc, 0, pf0);
@@ -410,14 +424,13 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     if (u >= n_full) mask(nxt, tn, u * BN);
     rowmax(nxt, mx);
     pv(tc, 1, pf1);
-    l_run[0] += ls[0];
-    l_run[1] += ls[1];
+    add_ls(ls);
     return grows();
   };
   // move the reference max (rare): O and l of the rows scale by exp2(old - new)
   auto rescale = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       const float m_new = fmaxf(m_ref[rb], max_xor32(mx[rb]));
       const float alpha = (m_ref[rb] == -INFINITY) ? 0.f : exp2f(m_ref[rb] - m_new);
       l_run[rb] *= alpha;
@@ -433,7 +446,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   for (int i = 0; i < PREF; ++i)
     if (i < n_wg) issue(i);
 
-  f32x16 sa[2], sb[2];
+  f32x16 sa[RB], sb[RB];
   int t = 0;  // the tile whose scores are in sa
   if (n_vis > 0) {
     wait_tile(0);
@@ -442,7 +455,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     rowmax(sa, mx);
     // first keys: O and l are still zero, only the reference is set
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) m_ref[rb] = max_xor32(mx[rb]);
+    for (int rb = 0; rb < RB; ++rb) m_ref[rb] = max_xor32(mx[rb]);
     // The hot loop runs two steps per trip so the score buffers alternate
     // without copies; a reference move (rare) rescales O and l in place.
     while (t + 2 < n_vis) {
@@ -453,20 +466,19 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     if (t + 1 < n_vis) {
       if (step(sa, sb, t)) rescale();
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) sa[rb] = sb[rb];
+      for (int rb = 0; rb < RB; ++rb) sa[rb] = sb[rb];
       t += 1;
     }
     // the last visible tile: exponentials and PV only
     {
-      float ls[2] = {0.f, 0.f};
-      bf16x8 pf0[2], pf1[2];
+      float ls[RB] = {};
+      bf16x8 pf0[RB], pf1[RB];
       const char *tc = stage(t);
       probs(sa, 0, pf0, ls);
       pv(tc, 0, pf0);
       probs(sa, 1, pf1, ls);
       pv(tc, 1, pf1);
-      l_run[0] += ls[0];
-      l_run[1] += ls[1];
+      add_ls(ls);
     }
     ++t;
   }
@@ -474,9 +486,9 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   for (; t < n_wg; ++t) wait_tile(t);
 
   // ---- epilogue: normalise; O^T -> LDS -> whole output rows
-  float inv[2], lse[2];
+  float inv[RB], lse[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = sum_xor32(l_run[rb]);
     const bool any = l_tot > 0.f;
     inv[rb] = any ? 1.f / l_tot : 0.f;
@@ -487,7 +499,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   constexpr int OPITCH = DV * OSZ + 16;        // row pitch of the staging area
   static_assert(NW * 32 * OPITCH <= NBUF * C::STAGE * 16, "staging fits the stages");
   char *ost = (char *)sm + w * 32 * OPITCH;    // 32 rows per wave per pass
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     // this lane: row n of block rb, dv = 32*b + 8*(i/4) + 4*hf + (i%4)
 #pragma unroll
     for (int b = 0; b < OB; ++b)
@@ -533,21 +545,26 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
 }
 
 template <int DQK, int DV>
-hipError_t launch(const AttnParams &p, const LaunchSegs &L, hipStream_t stream) {
+hipError_t launch(const AttnParams &p, const LaunchSegs &L, int tile_rows, hipStream_t stream) {
   const dim3 grid((unsigned)(L.num_tiles * p.hq));
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV>), grid, dim3(NT), 0, stream, p, L);
+  if (tile_rows == 32 * NW)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 1>), grid, dim3(NT), 0, stream, p, L);
+  else if (tile_rows == 64 * NW)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 2>), grid, dim3(NT), 0, stream, p, L);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_bf16_tile_rows(int, int) { return BM; }
+int attn_bf16_tile_rows(int, int, bool small) { return small ? 32 * NW : 64 * NW; }
 
-hipError_t launch_attn_bf16(const AttnParams &p, const LaunchSegs &L, int dqk,
-                            int dv, hipStream_t stream) {
-  if (dqk == 128 && dv == 128) return launch<128, 128>(p, L, stream);
-  if (dqk == 192 && dv == 128) return launch<192, 128>(p, L, stream);
-  if (dqk == 64 && dv == 64) return launch<64, 64>(p, L, stream);
+hipError_t launch_attn_bf16(const AttnParams &p, const LaunchSegs &L, int dqk, int dv,
+                            int tile_rows, hipStream_t stream) {
+  if (dqk == 128 && dv == 128) return launch<128, 128>(p, L, tile_rows, stream);
+  if (dqk == 192 && dv == 128) return launch<192, 128>(p, L, tile_rows, stream);
+  if (dqk == 64 && dv == 64) return launch<64, 64>(p, L, tile_rows, stream);
   return hipErrorInvalidValue;
 }
 

@@ -124,6 +124,10 @@ AttnParams make_params(const cp_attn_args &a) {
   return p;
 }
 
+// Below this many 256-row workgroups a bf16 call uses 128-row workgroups
+// (two per compute unit of the 256).
+constexpr int64_t kSmallGridWorkgroups = 512;
+
 // Splits the non-empty segments into launches of at most kMaxLaunchSegs,
 // heaviest first (largest visible KV extent), numbering their tiles.
 std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
@@ -296,11 +300,21 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
     }
     return fill_empty_segments(a, s);
   }
-  const int tile_rows = path == Path::F32 ? attn_f32_tile_rows(a->dqk)
-                                          : attn_bf16_tile_rows(a->dqk, a->dv);
+  int tile_rows = 0;
+  if (path == Path::F32) {
+    tile_rows = attn_f32_tile_rows(a->dqk);
+  } else {
+    // workgroups with 256-row tiles; fewer than two per compute unit -> 128-row tiles
+    const int big = attn_bf16_tile_rows(a->dqk, a->dv, false);
+    int64_t wgs = 0;
+    for (int32_t i = 0; i < a->num_segs; ++i)
+      if (a->segs[i].kv_end > a->segs[i].kv_begin)
+        wgs += static_cast<int64_t>((a->segs[i].q_end - a->segs[i].q_begin + big - 1) / big) * a->hq;
+    tile_rows = attn_bf16_tile_rows(a->dqk, a->dv, wgs < kSmallGridWorkgroups);
+  }
   for (const LaunchSegs &L : plan_launches(*a, tile_rows)) {
     hipError_t e = path == Path::F32 ? launch_attn_f32(p, L, a->dqk, s)
-                                     : launch_attn_bf16(p, L, a->dqk, a->dv, s);
+                                     : launch_attn_bf16(p, L, a->dqk, a->dv, tile_rows, s);
     if (e != hipSuccess) return device_error(e);
   }
   return fill_empty_segments(a, s);

@@ -82,13 +82,15 @@ cp_status device_error(hipError_t e);
 
 // Kernel entry points (one translation unit each).  They enqueue on
 // `stream` and return the launch status.
-hipError_t launch_attn_bf16(const AttnParams &p, const LaunchSegs &L, int dqk,
-                            int dv, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams &p, const LaunchSegs &L, int dqk, int dv,
+                            int tile_rows, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams &p, const LaunchSegs &L, int d,
                            hipStream_t stream);
 hipError_t launch_attn_decode_mla(const AttnParams &p, const DecodeLaunch &D,
                                   hipStream_t stream);
-int attn_bf16_tile_rows(int dqk, int dv);
+// query rows per bf16 workgroup: 256, or 128 for calls too small to give
+// every compute unit two workgroups with 256-row tiles
+int attn_bf16_tile_rows(int dqk, int dv, bool small);
 int attn_f32_tile_rows(int d);
 
 hipError_t launch_lse_merge(int32_t parts, int64_t pairs, int32_t dv,
