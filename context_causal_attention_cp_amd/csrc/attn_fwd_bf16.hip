@@ -50,7 +50,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int NW = 4;          // waves
 constexpr int NT = 64 * NW;    // threads
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kRescale = 8.0f;
+constexpr float kRescale = 8.0f;   // exact mode: log2 headroom before the reference moves
+constexpr float kGrowMax = 64.0f;  // main mode: log2 headroom before the workgroup is flagged
 constexpr int kNoPos = -(1 << 30);
 
 __device__ inline void map_work(int id, int num_tiles, int hq, int hkv, int &tile_order, int &h) {
@@ -155,8 +156,17 @@ struct Cfg {
 };
 
 // RB = 32-row MFMA column blocks per wave: 2 (256-row workgroups) or 1
-// (128-row workgroups, for launches too small to fill the chip otherwise)
-template <int DQK, int DV, int RB>
+// (128-row workgroups, for launches too small to fill the chip otherwise).
+// EXACT = false: main pass; each row's softmax reference is the max of its
+//   first visible tile and never moves, so the accumulator is never rescaled
+//   (no VALU touches it inside the loop).  Probabilities stay finite and
+//   exact in relative terms while no score exceeds the reference by more than
+//   2^kGrowMax; a workgroup where one does writes a flag (p.ws, one int32 per
+//   workgroup of the launch).
+// EXACT = true: recomputes only the flagged workgroups (the others return at
+//   once), moving the reference with an in-place rescale whenever a row
+//   outgrows it by more than 2^kRescale.
+template <int DQK, int DV, int RB, bool EXACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   using C = Cfg<DQK, DV>;
@@ -165,6 +175,9 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   constexpr int KCH = C::KCH, VCH = C::VCH, KS = C::KS, OB = C::OB;
   constexpr int BN = C::BN, NBUF = C::NBUF, PREF = C::PREF;
   __shared__ __attribute__((aligned(1024))) u32x4 sm[C::NBUF][C::STAGE];
+  __shared__ int s_flag;
+  int32_t *const flags = (int32_t *)p.ws;
+  if (EXACT && flags[blockIdx.x] == 0) return;
 
   const int tid = threadIdx.x;
   // the wave index is uniform per wave: say so, so that everything derived
@@ -175,6 +188,10 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   int tile_order, h;
   map_work(blockIdx.x, L.num_tiles, p.hq, p.hkv, tile_order, h);
   if (tile_order >= L.num_tiles) return;
+  if (!EXACT) {
+    if (tid == 0) s_flag = 0;
+    __syncthreads();
+  }
   const SegDesc sd = L.s[find_seg(L, tile_order)];
   const int ntile_q = (sd.q_len + BM - 1) / BM;
   const int tq = ntile_q - 1 - (tile_order - sd.tile_begin);
@@ -400,7 +417,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   auto grows = [&]() {
     bool g = false;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) g = g || (mx[rb] > m_ref[rb] + kRescale);
+    for (int rb = 0; rb < RB; ++rb) g = g || (mx[rb] > m_ref[rb] + (EXACT ? kRescale : kGrowMax));
     return __builtin_amdgcn_ballot_w64(g) != 0;
   };
   auto add_ls = [&](const float (&ls)[RB]) {
@@ -458,13 +475,19 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     for (int rb = 0; rb < RB; ++rb) m_ref[rb] = max_xor32(mx[rb]);
     // The hot loop runs two steps per trip so the score buffers alternate
     // without copies; a reference move (rare) rescales O and l in place.
+    // main pass: a row that outgrew its reference flags the workgroup (this
+    // tile's probabilities may be out of range; the exact pass redoes it)
+    auto outgrown = [&]() {
+      if (EXACT) rescale();
+      else if (lane == 0) s_flag = 1;
+    };
     while (t + 2 < n_vis) {
-      if (step(sa, sb, t)) rescale();
-      if (step(sb, sa, t + 1)) rescale();
+      if (step(sa, sb, t)) outgrown();
+      if (step(sb, sa, t + 1)) outgrown();
       t += 2;
     }
     if (t + 1 < n_vis) {
-      if (step(sa, sb, t)) rescale();
+      if (step(sa, sb, t)) outgrown();
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) sa[rb] = sb[rb];
       t += 1;
@@ -494,7 +517,8 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     inv[rb] = any ? 1.f / l_tot : 0.f;
     lse[rb] = any ? (m_ref[rb] + log2f(l_tot)) * kLn2 : -INFINITY;
   }
-  __syncthreads();  // every wave is done with the tiles
+  __syncthreads();  // every wave is done with the tiles (and its flag is in)
+  if (!EXACT && tid == 0) flags[blockIdx.x] = s_flag;
   constexpr int OSZ = 4;                       // bytes per staged element (fp32)
   constexpr int OPITCH = DV * OSZ + 16;        // row pitch of the staging area
   static_assert(NW * 32 * OPITCH <= NBUF * C::STAGE * 16, "staging fits the stages");
@@ -544,16 +568,22 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   }
 }
 
+// main pass, then the exact pass over the workgroups it flagged
+template <int DQK, int DV, int RB>
+hipError_t launch_rb(const AttnParams &p, const LaunchSegs &L, hipStream_t stream) {
+  const dim3 grid((unsigned)(L.num_tiles * p.hq));
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, RB, false>), grid, dim3(NT), 0, stream, p, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, RB, true>), grid, dim3(NT), 0, stream, p, L);
+  return hipGetLastError();
+}
+
 template <int DQK, int DV>
 hipError_t launch(const AttnParams &p, const LaunchSegs &L, int tile_rows, hipStream_t stream) {
-  const dim3 grid((unsigned)(L.num_tiles * p.hq));
-  if (tile_rows == 32 * NW)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 1>), grid, dim3(NT), 0, stream, p, L);
-  else if (tile_rows == 64 * NW)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, 2>), grid, dim3(NT), 0, stream, p, L);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (tile_rows == 32 * NW) return launch_rb<DQK, DV, 1>(p, L, stream);
+  if (tile_rows == 64 * NW) return launch_rb<DQK, DV, 2>(p, L, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -128,8 +128,28 @@ AttnParams make_params(const cp_attn_args &a) {
 // (two per compute unit of the 256).
 constexpr int64_t kSmallGridWorkgroups = 512;
 
+// Rows per workgroup of a bf16 call: 256, or 128 when the 256-row tiles
+// would give fewer than kSmallGridWorkgroups workgroups.
+int bf16_tile_rows(const cp_attn_args &a) {
+  const int big = attn_bf16_tile_rows(a.dqk, a.dv, false);
+  int64_t wgs = 0;
+  for (int32_t i = 0; i < a.num_segs; ++i)
+    if (a.segs[i].kv_end > a.segs[i].kv_begin)
+      wgs += static_cast<int64_t>((a.segs[i].q_end - a.segs[i].q_begin + big - 1) / big) * a.hq;
+  return attn_bf16_tile_rows(a.dqk, a.dv, wgs < kSmallGridWorkgroups);
+}
+
 // Splits the non-empty segments into launches of at most kMaxLaunchSegs,
 // heaviest first (largest visible KV extent), numbering their tiles.
+std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows);
+
+// bf16 workspace: one int32 flag per workgroup of every launch, 16-byte rounded
+size_t bf16_flag_bytes(const cp_attn_args &a, const std::vector<LaunchSegs> &launches) {
+  int64_t wgs = 0;
+  for (const LaunchSegs &L : launches) wgs += static_cast<int64_t>(L.num_tiles) * a.hq;
+  return static_cast<size_t>((wgs * 4 + 15) / 16 * 16);
+}
+
 std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
   std::vector<int32_t> order;
   for (int32_t i = 0; i < a.num_segs; ++i)
@@ -274,7 +294,10 @@ extern "C" cp_status cp_attn_workspace_size(const cp_attn_args *a, size_t *bytes
   cp_status st = check_attn(a);
   if (st != CP_OK) return st;
   if (!bytes) return CP_ERR_ARG;
-  *bytes = pick_path(*a) == Path::DecodeMla ? plan_decode(*a, nullptr) : 0;
+  *bytes = 0;
+  const Path path = pick_path(*a);
+  if (path == Path::DecodeMla) *bytes = plan_decode(*a, nullptr);
+  if (path == Path::Bf16Mfma) *bytes = bf16_flag_bytes(*a, plan_launches(*a, bf16_tile_rows(*a)));
   return CP_OK;
 }
 
@@ -300,22 +323,26 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
     }
     return fill_empty_segments(a, s);
   }
-  int tile_rows = 0;
   if (path == Path::F32) {
-    tile_rows = attn_f32_tile_rows(a->dqk);
-  } else {
-    // workgroups with 256-row tiles; fewer than two per compute unit -> 128-row tiles
-    const int big = attn_bf16_tile_rows(a->dqk, a->dv, false);
-    int64_t wgs = 0;
-    for (int32_t i = 0; i < a->num_segs; ++i)
-      if (a->segs[i].kv_end > a->segs[i].kv_begin)
-        wgs += static_cast<int64_t>((a->segs[i].q_end - a->segs[i].q_begin + big - 1) / big) * a->hq;
-    tile_rows = attn_bf16_tile_rows(a->dqk, a->dv, wgs < kSmallGridWorkgroups);
+    for (const LaunchSegs &L : plan_launches(*a, attn_f32_tile_rows(a->dqk))) {
+      const hipError_t e = launch_attn_f32(p, L, a->dqk, s);
+      if (e != hipSuccess) return device_error(e);
+    }
+    return fill_empty_segments(a, s);
   }
-  for (const LaunchSegs &L : plan_launches(*a, tile_rows)) {
-    hipError_t e = path == Path::F32 ? launch_attn_f32(p, L, a->dqk, s)
-                                     : launch_attn_bf16(p, L, a->dqk, a->dv, tile_rows, s);
+  // bf16: each launch's workgroups get one int32 flag in the workspace
+  const int tile_rows = bf16_tile_rows(*a);
+  const std::vector<LaunchSegs> launches = plan_launches(*a, tile_rows);
+  const size_t need = bf16_flag_bytes(*a, launches);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return CP_ERR_SMALL_BUFFER;
+  if (need > 0 && !aligned16(a->workspace)) return CP_ERR_ARG;
+  AttnParams q = p;
+  int32_t *flags = static_cast<int32_t *>(a->workspace);
+  for (const LaunchSegs &L : launches) {
+    q.ws = flags;
+    const hipError_t e = launch_attn_bf16(q, L, a->dqk, a->dv, tile_rows, s);
     if (e != hipSuccess) return device_error(e);
+    flags += static_cast<int64_t>(L.num_tiles) * a->hq;
   }
   return fill_empty_segments(a, s);
 }

@@ -150,12 +150,13 @@ cp_status cp_restore_index(int32_t strategy, int32_t cp_size, int32_t num_reqs,
  * (int32, num_kv_rows entries) or NULL.  workspace is device memory of at
  * least cp_attn_workspace_size bytes (NULL if that size is 0).
  *
- * Supported: dtype CP_BF16 with (dqk, dv) in {(64,64), (128,128), (192,128)};
- * dtype CP_BF16 with (dqk, dv) = (576, 512), the MLA-absorbed latent, where
- * v must equal k with equal strides (V is the first 512 columns of each
- * latent row) -- this path splits each row's keys into slices and needs a
- * workspace; dtype CP_F32 with dqk = dv in {64, 128}.  o_dtype CP_BF16 or
- * CP_F32; hq % hkv == 0.
+ * Supported: dtype CP_BF16 with (dqk, dv) in {(64,64), (128,128), (192,128)}
+ * (needs a small workspace, see cp_attn_workspace_size); dtype CP_BF16 with
+ * (dqk, dv) = (576, 512), the MLA-absorbed latent, where v must equal k with
+ * equal strides (V is the first 512 columns of each latent row) -- this path
+ * splits each row's keys into slices and needs a workspace; dtype CP_F32
+ * with dqk = dv in {64, 128}.  o_dtype CP_BF16 or CP_F32; hq % hkv == 0;
+ * scale > 0 and finite.
  */
 typedef struct {
   int32_t dtype;        /* cp_dtype of q, k, v */
@@ -179,8 +180,13 @@ typedef struct {
 
 /*
  * cp_attn_workspace_size -- bytes of device workspace cp_attn_fwd needs for
- * these arguments (0 for most shapes; the many-heads decode path keeps its
- * split-KV partials there).  Only the shape fields and segs are read.
+ * these arguments.  bf16 (dqk, dv) in {(64,64), (128,128), (192,128)}: one
+ * int32 per workgroup, i.e. 4 bytes per head per 128 or 256 query rows of
+ * each segment (the kernel flags there the rare workgroups whose scores
+ * outgrow the softmax reference of their first tile, and recomputes them);
+ * the MLA-absorbed decode shape: its split-KV partials; fp32: 0.  Only the
+ * shape fields and segs are read.  The contents need no initialisation and
+ * are scratch after the call.
  * Errors: as cp_attn_fwd's argument checks.
  */
 cp_status cp_attn_workspace_size(const cp_attn_args *args, size_t *bytes);

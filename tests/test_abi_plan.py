@@ -211,8 +211,18 @@ def test_attn_segment_errors():
 
 
 def test_workspace_size_query():
-    assert _ws() == (_lib.CP_OK, 0)
+    # bf16: one int32 flag per workgroup; 2 segments of 4 rows x 4 heads = 8
+    assert _ws() == (_lib.CP_OK, 32)
+    assert _ws(hq=8, hkv=2, q_row_stride=1024, o_row_stride=1024, lse_row_stride=8) == (_lib.CP_OK, 64)
+    assert _ws(dtype=_lib.CP_F32, o_dtype=_lib.CP_F32) == (_lib.CP_OK, 0)
     assert _ws(hq=3)[0] == _lib.CP_ERR_ARG
+
+
+def test_attn_workspace_required():
+    # the bf16 path needs its flag workspace: refused before any launch
+    assert _fwd() == _lib.CP_ERR_SMALL_BUFFER
+    assert _fwd(workspace=FAKE, workspace_bytes=16) == _lib.CP_ERR_SMALL_BUFFER
+    assert _fwd(workspace=FAKE + 4, workspace_bytes=64) == _lib.CP_ERR_ARG   # misaligned
 
 
 def test_merge_arg_errors():

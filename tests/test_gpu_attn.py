@@ -135,3 +135,32 @@ def test_repeatable_bitwise():
     b = cp.attn_fwd(q, k, v, plan, 0.07)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("rows,hq,val", [(300, 4, 0.1), (300, 4, 0.5), (4096, 128, 0.5)],
+                         ids=["small-2^27", "small-2^138", "large-2^138"])
+def test_reference_growth(rows, hq, val):
+    """A key, in a late tile, far above every score of the first tile: with
+    q = 1 and keys 0 except key 900 = val (192 dims, scale 1) the row max
+    grows by 192*val*log2(e) in log2 units -- 2^27 (kept by the main pass) or
+    2^138 (beyond fp32 exp range: the workgroup is flagged and recomputed).
+    128-row and 256-row workgroups; the plain definition decides."""
+    n_kv, dqk, dv = 1000, 192, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(rows + hq)
+    q = torch.ones((rows, hq, dqk), device=DEV, dtype=torch.bfloat16)
+    k = torch.zeros((n_kv, hq, dqk), device=DEV, dtype=torch.bfloat16)
+    k[900] = val
+    v = torch.randn((n_kv, hq, dv), generator=g, device=DEV).to(torch.bfloat16)
+    # every row sees all keys (positions n_kv .. n_kv + rows - 1)
+    segs = [cp.Segment(0, 0, rows, n_kv, 1, 0, n_kv)]
+    say(f"reference growth rows={rows} hq={hq} val={val}")
+    o, lse = cp.attn_fwd(q, k, v, segs, 1.0)
+    torch.cuda.synchronize()
+    sample = sorted(set([0, 1, rows // 2, rows - 1]))
+    q64, k64, v64 = f64(q), f64(k), f64(v)
+    for h in sorted(set([0, hq - 1])):
+        ro, rl = ao.attend(q64[sample, h], k64[:, h], v64[:, h], [n_kv + i for i in sample],
+                           np.arange(n_kv), 1.0)
+        compare(f64(o[sample, h]), f64(lse[sample, h]), ro, rl, range(len(sample)), "bf16",
+                f"head {h}")
