@@ -210,7 +210,8 @@ def main():
     del kv, o_parts, l_parts
     torch.cuda.empty_cache()
     if not a.no_extra:
-        out["extra"] = {"zigzag_t131072_mla_direct": _direct(cp, w, q_loc, k, v, plan)}
+        out["extra"] = {"zigzag_t131072_mla_direct": _direct(cp, w, q_loc, k, v, plan),
+                        "restore_apply_k_t131072": _restore(cp, w, k)}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(w, q, k, v, plan, a.cpu_baseline_seconds)
     del q, k, v, q_loc
@@ -234,6 +235,24 @@ def _time_ms(fn, reps=5, warm=1):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / reps
+
+
+def _restore(cp, w, k):
+    """cp_restore_apply on the all-gathered K rows of the 131072-token MLA
+    prefill (rank-major zigzag order -> causal order; 131072 rows of
+    128 x 192 bf16 = 48 KiB).  HBM-bound: algorithmic bytes = rows read +
+    rows written + the index."""
+    import numpy as np
+    import torch
+    restore, _ = cp.restore_index("zigzag", w.cp_size, list(w.new_lens))
+    idx = torch.from_numpy(restore.astype(np.int32)).to(k.device)
+    dst = torch.empty_like(k)
+    ms = _time_ms(lambda: cp.restore_apply(idx, k, out=dst), reps=5)
+    by = 2 * k.numel() * k.element_size() + idx.numel() * 4
+    del dst
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "algorithmic_bytes": by, "GB/s": round(by / ms / 1e6, 1),
+            "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
 def _direct(cp, w, q_loc, k, v, plan):

@@ -20,8 +20,9 @@ CP_OK, CP_ERR_ARG, CP_ERR_UNSUPPORTED, CP_ERR_SMALL_BUFFER, CP_ERR_DEVICE = rang
 CP_ZIGZAG, CP_INTERLEAVE = 0, 1
 CP_F32, CP_BF16 = 0, 1
 
-EXPORTS = ("cp_shard_plan", "cp_restore_index", "cp_attn_workspace_size",
-           "cp_attn_fwd", "cp_lse_merge", "cp_status_str", "cp_last_error", "cp_version")
+EXPORTS = ("cp_shard_plan", "cp_restore_index", "cp_restore_apply", "cp_choose_pass",
+           "cp_ring_pad_len", "cp_attn_workspace_size", "cp_attn_fwd", "cp_lse_merge",
+           "cp_status_str", "cp_last_error", "cp_version")
 
 _STRATEGY = {"zigzag": CP_ZIGZAG, "interleave": CP_INTERLEAVE}
 
@@ -82,6 +83,14 @@ def _load():
                                   pi32, pi32, pi32, i32, pi32, pi32]
     lib.cp_restore_index.restype = i32
     lib.cp_restore_index.argtypes = [i32, i32, i32, pi32, pi32, i32, pi32]
+    lib.cp_restore_apply.restype = i32
+    lib.cp_restore_apply.argtypes = [vp, i64, vp, i64, i64, vp, i64, i64, vp]
+    lib.cp_choose_pass.restype = i32
+    lib.cp_choose_pass.argtypes = [i64, i64, i32, i32, pi32, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_double)]
+    lib.cp_ring_pad_len.restype = i32
+    lib.cp_ring_pad_len.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), i64,
+                                    ctypes.POINTER(ctypes.c_int64)]
     lib.cp_attn_workspace_size.restype = i32
     lib.cp_attn_workspace_size.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.cp_attn_fwd.restype = i32
@@ -322,3 +331,50 @@ def lse_merge(o_parts, lse_parts, out_dtype=None, o_out=None, lse_out=None, stre
     if s != CP_OK:
         raise CpError(s, "cp_lse_merge")
     return o_out, lse_out
+
+def restore_apply(index, src, out=None, stream=None):
+    """cp_restore_apply: out[i] = src[index[i]] row-wise on the GPU.  ``index``
+    int32 [n] on the device; ``src`` [rows, ...] with contiguous rows."""
+    torch = _torch()
+    if index.dtype != torch.int32 or index.dim() != 1 or not index.is_contiguous():
+        raise ValueError("index must be a contiguous int32 vector")
+    if src.dim() < 1 or not src[0:1].is_contiguous():
+        raise ValueError("src rows must be contiguous")
+    n = index.shape[0]
+    if out is None:
+        out = torch.empty((n,) + tuple(src.shape[1:]), device=src.device, dtype=src.dtype)
+    row_bytes = src[0:1].numel() * src.element_size() if src.shape[0] else 0
+    s = _lib.cp_restore_apply(index.data_ptr(), n, src.data_ptr(), src.shape[0],
+                              src.stride(0) * src.element_size(), out.data_ptr(),
+                              out.stride(0) * out.element_size(), row_bytes,
+                              ctypes.c_void_p(_stream_handle(stream)))
+    if s != CP_OK:
+        raise CpError(s, "cp_restore_apply")
+    return out
+
+
+PASS_KV, PASS_Q = 0, 1
+
+
+def choose_pass(new_tokens: int, cached_tokens: int, n_heads: int, n_kv_heads: int):
+    """cp_choose_pass: (pass, miss_rate, h) -- PASS_Q when the miss rate is
+    within 2 * n_kv_heads / n_heads, else PASS_KV; h is the printed empirical
+    score (h > 0 favours pass-KV)."""
+    p = ctypes.c_int32()
+    m, h = ctypes.c_double(), ctypes.c_double()
+    s = _lib.cp_choose_pass(new_tokens, cached_tokens, n_heads, n_kv_heads, ctypes.byref(p),
+                            ctypes.byref(m), ctypes.byref(h))
+    if s != CP_OK:
+        raise CpError(s, "cp_choose_pass")
+    return p.value, m.value, h.value
+
+
+def ring_pad_len(cp_size: int, cached_per_rank: Sequence[int], new_tokens: int) -> int:
+    """cp_ring_pad_len: max_i P_i + ceil(T / N)."""
+    arr = (ctypes.c_int64 * max(1, len(cached_per_rank)))(*cached_per_rank)
+    out = ctypes.c_int64()
+    s = _lib.cp_ring_pad_len(cp_size, arr if cached_per_rank else None, new_tokens,
+                             ctypes.byref(out))
+    if s != CP_OK:
+        raise CpError(s, "cp_ring_pad_len")
+    return out.value

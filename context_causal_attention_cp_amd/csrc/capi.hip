@@ -372,3 +372,21 @@ extern "C" cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads
                                   out_dtype == CP_BF16, lse_out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CP_OK : device_error(e);
 }
+
+extern "C" cp_status cp_restore_apply(const int32_t *index, int64_t n, const void *src,
+                                      int64_t src_rows, int64_t src_row_stride, void *dst,
+                                      int64_t dst_row_stride, int64_t row_bytes, void *stream) {
+  if (n < 0 || src_rows < 0 || row_bytes < 0) return CP_ERR_ARG;
+  if (n == 0 || row_bytes == 0) return CP_OK;
+  if (!index || !dst || (src_rows > 0 && !src)) return CP_ERR_ARG;
+  if (row_bytes % 16 != 0 || src_row_stride % 16 != 0 || dst_row_stride % 16 != 0)
+    return CP_ERR_ARG;
+  if (src_row_stride < row_bytes || dst_row_stride < row_bytes) return CP_ERR_ARG;
+  if (!aligned16(dst) || (src && !aligned16(src))) return CP_ERR_ARG;
+  if (row_bytes / 16 > INT32_MAX) return CP_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipError_t e = launch_restore_apply(index, n, src, src_rows, src_row_stride, dst,
+                                            dst_row_stride, row_bytes,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CP_OK : device_error(e);
+}

@@ -93,6 +93,10 @@ hipError_t launch_attn_decode_mla(const AttnParams &p, const DecodeLaunch &D,
 int attn_bf16_tile_rows(int dqk, int dv, bool small);
 int attn_f32_tile_rows(int d);
 
+hipError_t launch_restore_apply(const int32_t *index, int64_t n, const void *src, int64_t src_rows,
+                                int64_t src_stride, void *dst, int64_t dst_stride,
+                                int64_t row_bytes, hipStream_t stream);
+
 hipError_t launch_lse_merge(int32_t parts, int64_t pairs, int32_t dv,
                             const void *o_parts, int part_bf16,
                             int64_t o_part_stride, const float *lse_parts,

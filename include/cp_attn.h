@@ -11,6 +11,9 @@
  *   cp_restore_index  the permutation that puts the rank-major all-gathered
  *                     token order back into causal order.  "What is Context
  *                     Parallelism" (blog), sections 2.1 and 5.1.
+ *   cp_restore_apply  that permutation applied on the GPU (a row gather).
+ *   cp_choose_pass    pass-KV or pass-Q for a request mix, and
+ *   cp_ring_pad_len   the padded ring message length.  Same blog, section 3.5.
  *   cp_attn_fwd       causal attention of one rank's query rows against a KV
  *                     buffer (the gathered KV, one ring round's KV block, or
  *                     one decode shard), giving the normalised output O and
@@ -120,6 +123,53 @@ cp_status cp_shard_plan(int32_t strategy, int32_t cp_size, int32_t cp_rank,
 cp_status cp_restore_index(int32_t strategy, int32_t cp_size, int32_t num_reqs,
                            const int32_t *new_lens, int32_t *restore,
                            int32_t cap, int32_t *padded_local);
+
+/*
+ * cp_restore_apply -- device gather: dst row i = src row index[i], i < n
+ * ("What is Context Parallelism", section 2.1 engineering notes and section
+ * 5.1: the rank-major all-gathered buffer, gathered by the restore index,
+ * is in causal order).  Enqueued on `stream` (a hipStream_t, NULL = the
+ * default stream); the caller owns every buffer.
+ * In:  index   DEVICE int32[n]; an entry outside [0, src_rows) zero-fills
+ *              its dst row (nothing is read out of bounds);
+ *      src     DEVICE, src_rows rows of row_bytes bytes, src_row_stride
+ *              bytes apart;
+ *      dst     DEVICE, n rows, dst_row_stride bytes apart (must not overlap
+ *              src);
+ *      row_bytes, both strides and both base pointers: multiples of 16, each
+ *      stride >= row_bytes.
+ * Errors: CP_ERR_ARG (negative sizes, NULL pointers, alignment or stride),
+ * CP_ERR_DEVICE (launch failed).  n = 0 or row_bytes = 0 enqueues nothing.
+ */
+cp_status cp_restore_apply(const int32_t *index, int64_t n, const void *src, int64_t src_rows,
+                           int64_t src_row_stride, void *dst, int64_t dst_row_stride,
+                           int64_t row_bytes, void *stream);
+
+/*
+ * cp_choose_pass -- host only.  Which ring variant moves less data
+ * ("What is Context Parallelism", section 3.5, pass-KV / pass-Q switch):
+ * with miss rate T / (T + P), pass-Q when T / (T + P) <= 2 * n_kv_heads /
+ * n_heads (compared exactly in integers), else pass-KV.
+ * In:  new_tokens T >= 1, cached_tokens P >= 0 (each <= 2^48),
+ *      1 <= n_kv_heads <= n_heads.
+ * Out (each optional): *pass (cp_pass), *miss_rate, *h_score = the section's
+ *      empirical fit -1.059 ln T + 1.145 ln(T/(T+P)) + 12.112 (h > 0
+ *      favours pass-KV; informational, it does not decide *pass).
+ * Errors: CP_ERR_ARG.
+ */
+typedef enum { CP_PASS_KV = 0, CP_PASS_Q = 1 } cp_pass;
+cp_status cp_choose_pass(int64_t new_tokens, int64_t cached_tokens, int32_t n_heads,
+                         int32_t n_kv_heads, int32_t *pass, double *miss_rate, double *h_score);
+
+/*
+ * cp_ring_pad_len -- host only.  Length every rank pads its ring message to
+ * (same section: max_i P_i + ceil(T / N) with P_i the tokens cached on rank i
+ * and T the new tokens over N = cp_size ranks).
+ * In:  cp_size >= 1, cached_per_rank (host, cp_size entries >= 0),
+ *      new_tokens >= 0.  Out: *pad_len.  Errors: CP_ERR_ARG.
+ */
+cp_status cp_ring_pad_len(int32_t cp_size, const int64_t *cached_per_rank, int64_t new_tokens,
+                          int64_t *pad_len);
 
 /*
  * Arguments of cp_attn_fwd.

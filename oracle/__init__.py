@@ -10,4 +10,6 @@ It shares no code with the HIP library and does not import it.
   and the log-sum-exp merge, in NumPy float64.
 * ``scalar_oracle`` -- the same attention as scalar Python loops, for tiny
   shapes; it pins ``attn_oracle``.
+* ``select_oracle`` -- the pass-KV / pass-Q rule, ring message padding and
+  the restore gather.
 """

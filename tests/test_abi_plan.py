@@ -241,3 +241,60 @@ def test_merge_arg_errors():
     assert m(ops=1000) == _lib.CP_ERR_ARG        # parts overlap
     assert m(lps=7) == _lib.CP_ERR_ARG
     assert m(rows=0) == _lib.CP_OK               # nothing to do, nothing enqueued
+
+
+# ---------------------------------------------------------------- pass selection, ring padding,
+# restore gather argument checks
+from oracle import select_oracle as so  # noqa: E402
+
+
+def test_choose_pass_matches_oracle():
+    rng = np.random.default_rng(11)
+    cases = [(1, 131071, 128, 8), (16384, 114688, 128, 8), (16385, 114687, 128, 8),
+             (131072, 0, 128, 8), (131072, 0, 8, 8), (7, 0, 32, 8), (100, 1 << 40, 64, 1)]
+    cases += [(int(rng.integers(1, 1 << 20)), int(rng.integers(0, 1 << 22)),
+               int(h), int(k)) for h, k in [(128, 8), (32, 8), (64, 4), (16, 16)] * 25]
+    for T, P, nh, nkv in cases:
+        p, m, h = cp.choose_pass(T, P, nh, nkv)
+        assert p == so.choose_pass(T, P, nh, nkv), (T, P, nh, nkv)
+        assert m == float(so.miss_rate(T, P))
+        assert abs(h - so.h_score(T, P)) <= 1e-9 * max(1.0, abs(h))
+
+
+def test_choose_pass_errors():
+    L = _lib._lib
+    p = ctypes.c_int32()
+    for args in [(0, 5, 8, 8), (1, -1, 8, 8), (1, 0, 0, 1), (1, 0, 8, 0), (1, 0, 4, 8), (1 << 50, 0, 8, 8)]:
+        assert L.cp_choose_pass(*args, ctypes.byref(p), None, None) == _lib.CP_ERR_ARG, args
+    assert L.cp_choose_pass(5, 0, 8, 8, None, None, None) == _lib.CP_OK
+
+
+def test_ring_pad_len_matches_oracle():
+    assert cp.ring_pad_len(3, [100, 300, 200], 10) == so.ring_pad_len([100, 300, 200], 10) == 304
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        N = int(rng.integers(1, 17))
+        Ps = [int(x) for x in rng.integers(0, 1 << 30, size=N)]
+        T = int(rng.integers(0, 1 << 30))
+        assert cp.ring_pad_len(N, Ps, T) == so.ring_pad_len(Ps, T)
+    L = _lib._lib
+    out = ctypes.c_int64()
+    arr = (ctypes.c_int64 * 2)(1, -1)
+    assert L.cp_ring_pad_len(2, arr, 3, ctypes.byref(out)) == _lib.CP_ERR_ARG
+    assert L.cp_ring_pad_len(0, arr, 3, ctypes.byref(out)) == _lib.CP_ERR_ARG
+    assert L.cp_ring_pad_len(2, None, 3, ctypes.byref(out)) == _lib.CP_ERR_ARG
+
+
+def test_restore_apply_arg_errors():
+    L = _lib._lib
+    def ra(idx=FAKE, n=4, src=FAKE, rows=8, ss=64, dst=FAKE, ds=64, rb=64):
+        return L.cp_restore_apply(idx, n, src, rows, ss, dst, ds, rb, None)
+    assert ra(n=-1) == _lib.CP_ERR_ARG
+    assert ra(idx=0) == _lib.CP_ERR_ARG
+    assert ra(dst=0) == _lib.CP_ERR_ARG
+    assert ra(rb=24) == _lib.CP_ERR_ARG          # not a multiple of 16
+    assert ra(ss=48) == _lib.CP_ERR_ARG          # stride below the row
+    assert ra(ds=72) == _lib.CP_ERR_ARG
+    assert ra(dst=FAKE + 8) == _lib.CP_ERR_ARG   # misaligned
+    assert ra(n=0) == _lib.CP_OK                 # nothing to do, nothing enqueued
+    assert ra(rb=0) == _lib.CP_OK
