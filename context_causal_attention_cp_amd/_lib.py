@@ -61,6 +61,7 @@ class AttnArgs(ctypes.Structure):
         ("segs", ctypes.POINTER(Segment)), ("num_segs", ctypes.c_int32),
         ("kv_pos", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("accumulate", ctypes.c_int32),
     ]
 
 
@@ -238,7 +239,7 @@ def _check_3d(name, t, rows_dim=None):
 
 
 def attn_args(q, k, v, segs, scale: float, o, lse, causal: bool = True, kv_pos=None,
-              workspace=None):
+              workspace=None, accumulate: bool = False):
     """Fill an AttnArgs from tensors (no call)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         _check_3d(name, t)
@@ -269,6 +270,7 @@ def attn_args(q, k, v, segs, scale: float, o, lse, causal: bool = True, kv_pos=N
     a.lse, a.lse_row_stride = lse.data_ptr(), lse.stride(0)
     a.segs, a.num_segs = seg_arr, nseg
     a.kv_pos = kv_pos.data_ptr() if kv_pos is not None else None
+    a.accumulate = 1 if accumulate else 0
     if workspace is not None:
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return a, seg_arr
@@ -283,18 +285,21 @@ def attn_workspace_size(a: AttnArgs) -> int:
 
 
 def attn_fwd(q, k, v, segs, scale: float, causal: bool = True, kv_pos=None, o=None,
-             lse=None, o_dtype=None, workspace=None, stream=None):
+             lse=None, o_dtype=None, workspace=None, stream=None, accumulate: bool = False):
     """cp_attn_fwd.  Returns (o [rows, hq, dv], lse fp32 [rows, hq]).
 
     Outputs are allocated with torch.empty when not given (rows that no
-    segment covers are left as allocated)."""
+    segment covers are left as allocated).  accumulate=True merges each row's
+    new partial into the (o, lse) given (lse = -inf: empty accumulator)."""
+    if accumulate and (o is None or lse is None):
+        raise ValueError("accumulate needs the running o and lse")
     torch = _torch()
     if o is None:
         o = torch.empty((q.shape[0], q.shape[1], v.shape[2]), device=q.device,
                         dtype=o_dtype if o_dtype is not None else q.dtype)
     if lse is None:
         lse = torch.empty((q.shape[0], q.shape[1]), device=q.device, dtype=torch.float32)
-    a, keep = attn_args(q, k, v, segs, scale, o, lse, causal, kv_pos, workspace)
+    a, keep = attn_args(q, k, v, segs, scale, o, lse, causal, kv_pos, workspace, accumulate)
     need = attn_workspace_size(a)
     if need and (workspace is None or a.workspace_bytes < need):
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)

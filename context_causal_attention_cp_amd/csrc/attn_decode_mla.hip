@@ -368,7 +368,36 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const AttnPara
       acc[4] += wgt * b.x; acc[5] += wgt * b.y; acc[6] += wgt * b.z; acc[7] += wgt * b.w;
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  float lse_out = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+  if (p.accumulate) {
+    // merge into the running (O, LSE) of this (row, head): an empty new
+    // partial leaves it; an empty accumulator (LSE = -inf) is replaced
+    if (!(wsum > 0.f)) return;
+    const float la = p.lse[qrow * p.lse_rs + h];
+    if (la != -INFINITY) {
+      const float mm = fmaxf(la, lse_out);
+      const float wa = expf(la - mm), wn = expf(lse_out - mm);
+      const float winv = 1.f / (wa + wn);
+      float oa[8];
+      if (p.o_bf16) {
+        const u32x4 v = *(const u32x4 *)((const __bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + lane * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          oa[2 * i] = __uint_as_float(v[i] << 16);
+          oa[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+      } else {
+        const float *op = (const float *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + lane * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) oa[i] = op[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = (wa * oa[i] + wn * acc[i] * inv) * winv;
+      inv = 1.f;
+      lse_out = mm + logf(wa + wn);
+    }
+  }
   if (p.o_bf16) {
     __bf16 *op = (__bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + lane * 8;
     u32x4 v;
@@ -380,7 +409,7 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const AttnPara
     *(float4 *)op = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
     *(float4 *)(op + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   }
-  if (lane == 0) p.lse[qrow * p.lse_rs + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+  if (lane == 0) p.lse[qrow * p.lse_rs + h] = lse_out;
 }
 
 }  // namespace

@@ -125,6 +125,46 @@ __device__ inline void wait_later(int later) {
   wait_vm<0>();
 }
 
+// Accumulate mode: merge a row's new normalised partial (8 elements a, c at
+// dv offset d0, log-sum-exp ln) into the running (O, LSE) of that row in
+// p.o / p.lse, in place: m = max(la, ln), w = exp(l - m),
+// O = (wa Oa + wn On) / (wa + wn), L = m + ln(wa + wn).  la = -inf means an
+// empty accumulator (Oa not read).  Returns false if ln = -inf (nothing to
+// merge: the row is left as it is).  The lane with write_lse stores L.
+__device__ inline bool merge_into(const AttnParams &p, int64_t qrow, int h, int d0, float ln,
+                                  bool write_lse, float4 &a, float4 &c) {
+  if (ln == -INFINITY) return false;
+  float *lp = p.lse + qrow * p.lse_rs + h;
+  const float la = *lp;
+  float lnew = ln;
+  if (la != -INFINITY) {
+    const float m = fmaxf(la, ln);
+    const float wa = expf(la - m), wn = expf(ln - m);
+    const float inv = 1.f / (wa + wn);
+    float oa[8];
+    if (p.o_bf16) {
+      const u32x4 v = *(const u32x4 *)((const __bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + d0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        oa[2 * i] = __uint_as_float(v[i] << 16);
+        oa[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+      }
+    } else {
+      const float *op = (const float *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + d0;
+      const float4 x = *(const float4 *)op, y = *(const float4 *)(op + 4);
+      oa[0] = x.x; oa[1] = x.y; oa[2] = x.z; oa[3] = x.w;
+      oa[4] = y.x; oa[5] = y.y; oa[6] = y.z; oa[7] = y.w;
+    }
+    a = make_float4((wa * oa[0] + wn * a.x) * inv, (wa * oa[1] + wn * a.y) * inv,
+                    (wa * oa[2] + wn * a.z) * inv, (wa * oa[3] + wn * a.w) * inv);
+    c = make_float4((wa * oa[4] + wn * c.x) * inv, (wa * oa[5] + wn * c.y) * inv,
+                    (wa * oa[6] + wn * c.z) * inv, (wa * oa[7] + wn * c.w) * inv);
+    lnew = m + logf(wa + wn);
+  }
+  if (write_lse) *lp = lnew;
+  return true;
+}
+
 // LDS layouts of one stage (16-byte units; keys fastest, so no swizzle):
 //   K  unit ((key/16)*KCH + chunk)*16 + key%16   -- a K fragment read (32 keys
 //      of one chunk) is 2 x 256 contiguous bytes;
@@ -176,6 +216,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   constexpr int BN = C::BN, NBUF = C::NBUF, PREF = C::PREF;
   __shared__ __attribute__((aligned(1024))) u32x4 sm[C::NBUF][C::STAGE];
   __shared__ int s_flag;
+  __shared__ float s_lse[NW * 32];  // epilogue: the new log-sum-exp of each staged row
   int32_t *const flags = (int32_t *)p.ws;
   if (EXACT && flags[blockIdx.x] == 0) return;
 
@@ -528,7 +569,11 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     lse[rb] = any ? (m_ref[rb] + log2f(l_tot)) * kLn2 : -INFINITY;
   }
   __syncthreads();  // every wave is done with the tiles (and its flag is in)
-  if (!EXACT && tid == 0) flags[blockIdx.x] = s_flag;
+  if (!EXACT) {
+    const int flagged = s_flag;
+    if (tid == 0) flags[blockIdx.x] = flagged;
+    if (flagged) return;  // the exact pass writes (or merges) these rows
+  }
   constexpr int OSZ = 4;                       // bytes per staged element (fp32)
   constexpr int OPITCH = DV * OSZ + 16;        // row pitch of the staging area
   static_assert(NW * 32 * OPITCH <= NBUF * C::STAGE * 16, "staging fits the stages");
@@ -543,7 +588,8 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
                                oacc[b][rb][4 * g + 2] * inv[rb], oacc[b][rb][4 * g + 3] * inv[rb]);
         *(float4 *)(ost + n * OPITCH + (32 * b + 8 * g + 4 * hf) * OSZ) = x;
       }
-    if (hf == 0 && valid[rb]) {
+    if (hf == 0) s_lse[w * 32 + n] = lse[rb];
+    if (!p.accumulate && hf == 0 && valid[rb]) {
       const int64_t qrow = (int64_t)sd.q_begin + row0 + w * RW + rb * 32 + n;
       p.lse[qrow * p.lse_rs + h] = lse[rb];
     }
@@ -557,9 +603,11 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
       const int r = r0 + rsub;
       const int rr = w * RW + rb * 32 + r;
       if (rr < rows_here) {
-        const float4 a = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ);
-        const float4 c = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ + 16);
+        float4 a = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ);
+        float4 c = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ + 16);
         const int64_t qrow = (int64_t)sd.q_begin + row0 + rr;
+        if (p.accumulate && !merge_into(p, qrow, h, sub * 8, s_lse[w * 32 + r], sub == 0, a, c))
+          continue;  // no visible key in this call: the accumulator row stays
         if (p.o_bf16) {
           u32x4 v;
           v[0] = pack_bf16(a.x, a.y);

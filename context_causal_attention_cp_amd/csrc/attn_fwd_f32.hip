@@ -98,8 +98,28 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const AttnParams p, co
   }
   if (!valid) return;
   const bool any = l > 0.f;
-  const float inv = any ? 1.f / l : 0.f;
-  p.lse[qrow * p.lse_rs + h] = any ? m + logf(l) : -INFINITY;
+  float inv = any ? 1.f / l : 0.f;
+  float lse = any ? m + logf(l) : -INFINITY;
+  if (p.accumulate) {
+    // merge into the running (O, LSE) of this row: an empty new partial
+    // leaves it; an empty accumulator (LSE = -inf) is replaced
+    if (!any) return;
+    const float la = p.lse[qrow * p.lse_rs + h];
+    if (la != -INFINITY) {
+      const float mm = fmaxf(la, lse);
+      const float wa = expf(la - mm), wn = expf(lse - mm);
+      const float winv = 1.f / (wa + wn);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const float oa = p.o_bf16 ? (float)((const __bf16 *)p.o)[qrow * p.o_rs + (int64_t)h * p.o_hs + d]
+                                  : ((const float *)p.o)[qrow * p.o_rs + (int64_t)h * p.o_hs + d];
+        o[d] = (wa * oa + wn * o[d] * inv) * winv;
+      }
+      inv = 1.f;
+      lse = mm + logf(wa + wn);
+    }
+  }
+  p.lse[qrow * p.lse_rs + h] = lse;
   if (p.o_bf16) {
     __bf16 *op = (__bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs;
 #pragma unroll

@@ -44,6 +44,7 @@ cp_status check_attn(const cp_attn_args *a) {
   if (a->dtype != CP_BF16 && a->dtype != CP_F32) return CP_ERR_UNSUPPORTED;
   if (a->o_dtype != CP_BF16 && a->o_dtype != CP_F32) return CP_ERR_UNSUPPORTED;
   if (a->num_q_rows < 0 || a->num_kv_rows < 0 || a->num_segs < 0) return CP_ERR_ARG;
+  if (a->accumulate != 0 && a->accumulate != 1) return CP_ERR_ARG;
   if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv != 0) return CP_ERR_ARG;
   if (a->dqk < 1 || a->dv < 1) return CP_ERR_ARG;
   if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return CP_ERR_ARG;
@@ -119,6 +120,7 @@ AttnParams make_params(const cp_attn_args &a) {
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.causal = a.causal ? 1 : 0;
   p.o_bf16 = a.o_dtype == CP_BF16;
+  p.accumulate = a.accumulate ? 1 : 0;
   p.ws = a.workspace;
   p.ws_bytes = static_cast<int64_t>(a.workspace_bytes);
   return p;
@@ -246,6 +248,7 @@ __global__ void fill_empty_rows(float *lse, int64_t lse_rs, void *o, int64_t o_r
 
 // Segments that see no KV row at all get O = 0, LSE = -inf.
 cp_status fill_empty_segments(const cp_attn_args *a, hipStream_t s) {
+  if (a->accumulate) return CP_OK;  // an empty partial leaves the accumulator as it is
   for (int32_t i = 0; i < a->num_segs; ++i) {
     const cp_segment &g = a->segs[i];
     const int32_t n = g.q_end - g.q_begin;

@@ -53,6 +53,7 @@ struct AttnParams {
   float scale_log2;   // scale * log2(e)
   int32_t causal;
   int32_t o_bf16;     // 1: o is bf16, 0: fp32
+  int32_t accumulate; // 1: merge into the (O, LSE) already in o / lse
   void *ws;           // workspace (device)
   int64_t ws_bytes;
 };

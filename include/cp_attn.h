@@ -192,6 +192,16 @@ cp_status cp_ring_pad_len(int32_t cp_size, const int64_t *cached_per_rank, int64
  * A row with no visible key gets o = 0 and lse = -inf.
  * Rows not covered by any segment are not written.
  *
+ * accumulate = 1 (the pass-Q running accumulator, same blog section 3.3 and
+ * the merge of section 3.6 fused into the epilogue): o and lse already hold
+ * a running result (O_acc, L_acc) of the same rows; each row's new partial
+ * (O_new, L_new) over this call's keys is merged into it -- m = max(L_acc,
+ * L_new), w = exp(L - m), O = (w_acc O_acc + w_new O_new) / (w_acc + w_new),
+ * L = m + ln(w_acc + w_new) -- and written back.  A row whose new partial is
+ * empty (no visible key) is left untouched; L_acc = -inf marks an empty
+ * accumulator row (its O_acc is not read), so a sequence of calls starts
+ * from lse = -inf or from a first call with accumulate = 0.
+ *
  * Preconditions the library cannot check (violations give unspecified
  * values, never an out-of-bounds access): each row is in at most one
  * segment; kv_pos is strictly increasing over every segment's kv range.
@@ -226,6 +236,7 @@ typedef struct {
   const int32_t *kv_pos;   /* device, optional */
   void *workspace;         /* device, optional */
   size_t workspace_bytes;
+  int32_t accumulate;      /* 0: write (O, LSE); 1: merge into the (O, LSE) in o / lse */
 } cp_attn_args;
 
 /*

@@ -191,6 +191,7 @@ def _ws(**kw):
     (dict(q=FAKE + 8), _lib.CP_ERR_ARG),               # misaligned
     (dict(k_row_stride=250), _lib.CP_ERR_ARG),         # stride not a multiple of 8
     (dict(o_head_stride=130), _lib.CP_ERR_ARG),
+    (dict(accumulate=2), _lib.CP_ERR_ARG),
 ])
 def test_attn_arg_errors(kw, want):
     assert _fwd(**kw) == want

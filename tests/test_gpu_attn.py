@@ -164,3 +164,38 @@ def test_reference_growth(rows, hq, val):
                            np.arange(n_kv), 1.0)
         compare(f64(o[sample, h]), f64(lse[sample, h]), ro, rl, range(len(sample)), "bf16",
                 f"head {h}")
+
+
+@pytest.mark.parametrize("dqk,dv,dtype,odt,C,T,H", [
+    (192, 128, "bf16", torch.float32, 4, 640, 2),     # 128-row workgroups
+    (128, 128, "bf16", torch.bfloat16, 4, 640, 2),
+    (192, 128, "bf16", torch.float32, 2, 2048, 128),  # 256-row workgroups
+    (64, 64, "f32", torch.float32, 4, 256, 4),        # fp32 kernel
+], ids=["192-f32acc", "128-bf16acc", "192-f32acc-256rows", "fp32"])
+def test_ring_accumulate_in_place(dqk, dv, dtype, odt, C, T, H):
+    """Pass-Q style running accumulator: the C ring partials of a rank merged
+    in the attention epilogue (accumulate=1), starting from an empty (LSE =
+    -inf) accumulator, must equal the dense attention of the rank's rows;
+    partial calls whose rows see no key leave the accumulator untouched."""
+    q, k, v = _tensors(T, T, H, H, dqk, dv, dtype, seed=dqk + C)
+    q64, k64, v64 = f64(q), f64(k), f64(v)
+    scale = 1.0 / np.sqrt(dqk)
+    for r in sorted({0, C - 1}):
+        plan = cp.shard_plan("zigzag", C, r, [T], [0])
+        mine = plan.global_idx.astype(np.int64)
+        q_loc = q.index_select(0, torch.from_numpy(mine).to(DEV))
+        o = torch.full((len(mine), H, dv), 7.0, device=DEV, dtype=odt)   # not read while LSE = -inf
+        lse = torch.full((len(mine), H), -np.inf, device=DEV, dtype=torch.float32)
+        for j in reversed(range(C)):
+            say(f"accumulate d={dqk}/{dv} {dtype} rank {r} pair {j}")
+            rows_j = cp.shard_plan("zigzag", C, j, [T], [0]).global_idx.astype(np.int64)
+            idx = torch.from_numpy(rows_j).to(DEV)
+            segs = [cp.Segment(s.req, s.q_begin, s.q_end, s.pos_begin, s.pos_stride, 0, len(rows_j))
+                    for s in plan.segments]
+            cp.attn_fwd(q_loc, k.index_select(0, idx), v.index_select(0, idx), segs, scale,
+                        kv_pos=idx.to(torch.int32), o=o, lse=lse, accumulate=True)
+        torch.cuda.synchronize()
+        dense_o, dense_l = ao.shard_attention(q64[mine], k64, v64,
+                                              oracle_segments("zigzag", C, r, [T], [0]), H, H, scale)
+        compare(f64(o), f64(lse), dense_o, dense_l, range(len(mine)),
+                "bf16" if dtype == "bf16" else "f32", f"rank {r} accumulated")

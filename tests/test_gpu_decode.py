@@ -151,3 +151,29 @@ def test_decode_reference_growth(val):
     for b in range(B):
         ro, rl = _oracle_shard(q64, kv64, b, 0, 1, 1.0, ctx)
         compare(f64(o[b]), f64(l[b]), ro, rl, range(hq), "bf16", f"req {b}")
+
+
+def test_decode_accumulate_in_place():
+    """The W shard partials merged into a running (O, LSE) by the decode
+    combine (accumulate=1) instead of a separate merge."""
+    B, ctx, W, hq = 2, 2000, 4, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4242)
+    q = torch.randn((B, hq, DQK), generator=g, device=DEV).to(torch.bfloat16)
+    kv = torch.randn((B, ctx, DQK), generator=g, device=DEV).to(torch.bfloat16)
+    scale = 1.0 / np.sqrt(DQK)
+    o = torch.zeros((B, hq, DV), device=DEV, dtype=torch.float32)
+    lse = torch.full((B, hq), -np.inf, device=DEV, dtype=torch.float32)
+    for j in range(W):
+        say(f"decode accumulate shard {j}")
+        shard = kv[:, j::W].contiguous()
+        n_j = shard.shape[1]
+        k = shard.view(B * n_j, 1, DQK)
+        pos = torch.arange(j, ctx, W, device=DEV, dtype=torch.int32).repeat(B)
+        segs = [cp.Segment(b, b, b + 1, ctx, 1, b * n_j, (b + 1) * n_j) for b in range(B)]
+        cp.attn_fwd(q, k, k[:, :, :DV], segs, scale, kv_pos=pos, o=o, lse=lse, accumulate=True)
+    torch.cuda.synchronize()
+    q64, kv64 = f64(q), f64(kv)
+    for b in range(B):
+        ro, rl = ao.attend(q64[b], kv64[b], kv64[b, :, :DV], [ctx] * hq, np.arange(ctx), scale)
+        compare(f64(o[b]), f64(lse[b]), ro, rl, range(hq), "bf16", f"req {b} accumulated")
