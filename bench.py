@@ -224,6 +224,8 @@ def main():
         out["extra"]["zigzag_t8192_p1024"] = _prefill_ranks(cp, workloads.get("zigzag_t8192_p1024"))
         out["extra"]["interleave_b12"] = _prefill_ranks(cp, workloads.get("interleave_b12"))
         out["extra"]["decode_mla_b64"] = _decode(cp, workloads.get("decode_mla_b64"))
+        out["extra"]["decode_mla_b64_paged_block128"] = _decode_paged(
+            cp, workloads.get("decode_mla_b64"), 128)
     print(json.dumps(out), flush=True)
 
 
@@ -362,6 +364,53 @@ def _decode(cp, w):
             "merge_ms": round(mms, 4), "merge_GB/s": round(mby / mms / 1e6, 1),
             "merge_frac_hbm": round(mby / mms / 1e6 / PEAK_HBM_GBS, 4),
             "merge_note": "the partials (134 MB) fit the 256 MB Infinity Cache: effective rate"}
+
+
+def _decode_paged(cp, w, bs):
+    """Decode-CP rank 0 with the cache interleaved over the ranks in blocks
+    of ``bs`` tokens (token i on rank (i // bs) mod W), its blocks scattered
+    over a randomly allocated pool and read through a block table; the same
+    rows laid out contiguously are timed beside it."""
+    import numpy as np
+    import torch
+    import workloads
+    q, kv = workloads.decode_tensors(w, "cuda")
+    W, B, ctx = w.cp_size, w.num_reqs, w.ctx_len
+    i = np.arange(ctx)
+    keys = i[(i // bs) % W == 0]
+    n = len(keys)
+    table, pool_row, nblocks = workloads.paged_layout([n] * B, bs, 64, 2024)
+    src = torch.from_numpy((np.arange(B)[:, None] * ctx + keys[None, :]).reshape(-1)).cuda()
+    flat = kv.view(B * ctx, w.dqk)
+    pool = torch.zeros((nblocks * bs, 1, w.dqk), device="cuda", dtype=kv.dtype)
+    pool[torch.from_numpy(pool_row[:, :n].reshape(-1)).cuda(), 0] = flat[src]
+    kc = flat[src].view(B * n, 1, w.dqk)
+    del kv, flat
+    torch.cuda.empty_cache()
+    stride = table.shape[1]
+    pos = np.zeros((B, stride * bs), dtype=np.int32)
+    pos[:, :n] = keys
+    pos = torch.from_numpy(pos.reshape(-1)).cuda()
+    pos_c = torch.from_numpy(np.tile(keys, B).astype(np.int32)).cuda()
+    bt = torch.from_numpy(table).cuda()
+    o = torch.empty((B, w.hq, w.dv), device="cuda", dtype=torch.float32)
+    lse = torch.empty((B, w.hq), device="cuda", dtype=torch.float32)
+    segs_p = [cp.Segment(b, b, b + 1, ctx, 1, 0, n) for b in range(B)]
+    segs_c = [cp.Segment(b, b, b + 1, ctx, 1, b * n, (b + 1) * n) for b in range(B)]
+    a, keep = cp._lib.attn_args(q, pool, pool[:, :, :w.dv], segs_p, w.scale, o, lse, kv_pos=pos,
+                                block_table=bt, block_size=bs)
+    ws = torch.empty(cp.attn_workspace_size(a), device="cuda", dtype=torch.uint8)
+    paged = _time_ms(lambda: cp.attn_fwd(q, pool, pool[:, :, :w.dv], segs_p, w.scale, kv_pos=pos,
+                                         o=o, lse=lse, workspace=ws, block_table=bt,
+                                         block_size=bs), reps=10)
+    cont = _time_ms(lambda: cp.attn_fwd(q, kc, kc[:, :, :w.dv], segs_c, w.scale, kv_pos=pos_c,
+                                        o=o, lse=lse, workspace=ws), reps=10)
+    by = B * n * w.dqk * 2 + q.numel() * 2 + B * w.hq * (w.dv * 4 + 4)
+    return {"block_size": bs, "rank_rows_per_request": n, "paged_ms": round(paged, 4),
+            "contiguous_ms": round(cont, 4), "algorithmic_bytes": by,
+            "paged_GB/s": round(by / paged / 1e6, 1),
+            "paged_frac_hbm": round(by / paged / 1e6 / PEAK_HBM_GBS, 4),
+            "paged_over_contiguous": round(paged / cont, 4)}
 
 
 def _cpu_baseline(w, q, k, v, plan, budget_s):

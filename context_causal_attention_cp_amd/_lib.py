@@ -62,6 +62,8 @@ class AttnArgs(ctypes.Structure):
         ("kv_pos", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("accumulate", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
     ]
 
 
@@ -239,8 +241,13 @@ def _check_3d(name, t, rows_dim=None):
 
 
 def attn_args(q, k, v, segs, scale: float, o, lse, causal: bool = True, kv_pos=None,
-              workspace=None, accumulate: bool = False):
-    """Fill an AttnArgs from tensors (no call)."""
+              workspace=None, accumulate: bool = False, block_table=None, block_size: int = 0):
+    """Fill an AttnArgs from tensors (no call).
+
+    Paged KV: block_table int32 [requests, blocks per request] (rows
+    contiguous), k / v the pool of blocks of block_size rows; kv_pos, if
+    given, is int32 [requests * blocks per request * block_size] by logical
+    row."""
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         _check_3d(name, t)
     if k.shape[0] != v.shape[0] or k.shape[1] != v.shape[1] or q.shape[2] != k.shape[2]:
@@ -250,10 +257,16 @@ def attn_args(q, k, v, segs, scale: float, o, lse, causal: bool = True, kv_pos=N
     if lse.dim() != 2 or lse.shape[0] != q.shape[0] or lse.shape[1] != q.shape[1] or \
             lse.stride(1) != 1 or lse.dtype != _torch().float32:
         raise ValueError("lse must be fp32 [rows, hq] with contiguous heads")
+    kv_rows = k.shape[0]
+    if block_table is not None:
+        if block_table.dtype != _torch().int32 or block_table.dim() != 2 or \
+                block_table.stride(1) != 1:
+            raise ValueError("block_table must be int32 [requests, blocks] with contiguous rows")
+        kv_rows = block_table.shape[0] * block_table.stride(0) * int(block_size)
     if kv_pos is not None:
-        if kv_pos.dtype != _torch().int32 or kv_pos.dim() != 1 or kv_pos.shape[0] != k.shape[0] \
+        if kv_pos.dtype != _torch().int32 or kv_pos.dim() != 1 or kv_pos.shape[0] != kv_rows \
                 or not kv_pos.is_contiguous():
-            raise ValueError("kv_pos must be int32 [num_kv_rows], contiguous")
+            raise ValueError("kv_pos must be int32 [kv rows], contiguous")
     dt = _dtype_code(q)
     if _dtype_code(k) != dt or _dtype_code(v) != dt:
         raise TypeError("q, k, v must share a dtype")
@@ -271,6 +284,9 @@ def attn_args(q, k, v, segs, scale: float, o, lse, causal: bool = True, kv_pos=N
     a.segs, a.num_segs = seg_arr, nseg
     a.kv_pos = kv_pos.data_ptr() if kv_pos is not None else None
     a.accumulate = 1 if accumulate else 0
+    if block_table is not None:
+        a.block_table = block_table.data_ptr()
+        a.block_table_stride, a.block_size = block_table.stride(0), int(block_size)
     if workspace is not None:
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return a, seg_arr
@@ -285,12 +301,14 @@ def attn_workspace_size(a: AttnArgs) -> int:
 
 
 def attn_fwd(q, k, v, segs, scale: float, causal: bool = True, kv_pos=None, o=None,
-             lse=None, o_dtype=None, workspace=None, stream=None, accumulate: bool = False):
+             lse=None, o_dtype=None, workspace=None, stream=None, accumulate: bool = False,
+             block_table=None, block_size: int = 0):
     """cp_attn_fwd.  Returns (o [rows, hq, dv], lse fp32 [rows, hq]).
 
     Outputs are allocated with torch.empty when not given (rows that no
     segment covers are left as allocated).  accumulate=True merges each row's
-    new partial into the (o, lse) given (lse = -inf: empty accumulator)."""
+    new partial into the (o, lse) given (lse = -inf: empty accumulator).
+    block_table / block_size: paged KV (see attn_args)."""
     if accumulate and (o is None or lse is None):
         raise ValueError("accumulate needs the running o and lse")
     torch = _torch()
@@ -299,7 +317,8 @@ def attn_fwd(q, k, v, segs, scale: float, causal: bool = True, kv_pos=None, o=No
                         dtype=o_dtype if o_dtype is not None else q.dtype)
     if lse is None:
         lse = torch.empty((q.shape[0], q.shape[1]), device=q.device, dtype=torch.float32)
-    a, keep = attn_args(q, k, v, segs, scale, o, lse, causal, kv_pos, workspace, accumulate)
+    a, keep = attn_args(q, k, v, segs, scale, o, lse, causal, kv_pos, workspace, accumulate,
+                        block_table, block_size)
     need = attn_workspace_size(a)
     if need and (workspace is None or a.workspace_bytes < need):
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)

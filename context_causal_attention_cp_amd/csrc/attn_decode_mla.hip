@@ -26,6 +26,13 @@
 //     exchange row maxima (and rescale the accumulator) when some lane's
 //     tile max exceeds the reference by more than 2^8;
 // and writes the slice's normalised partial (O_s, LSE_s) to the workspace.
+//
+// Paged KV (the cache of a rank that holds whole blocks of tokens, section
+// 2.2's block interleave): the slice's block ids are staged in LDS once; a
+// 32-row tile never crosses a block (blocks are multiples of 32 rows and
+// segments start on a tile), so each tile gets its own buffer resource at
+// its block's pool row and the per-lane offsets stay those of a
+// contiguous tile.
 // A second kernel merges the slices of each (row, head) by LSE.
 #include <hip/hip_runtime.h>
 
@@ -121,9 +128,16 @@ __device__ inline void decode_item(const DecodeLaunch &D, int item, int &si, int
   row = rem / D.hkv;
 }
 
+template <bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
-  __shared__ __attribute__((aligned(1024))) u32x4 sk[NBUF][TILE_CH];
+  // key tiles, then (paged) the slice's block ids, in ONE LDS object: with a
+  // second LDS variable the waitcnt pass can no longer tell the tile reads
+  // from the in-flight LDS-DMA writes and drains them (vmcnt(0)) every tile
+  constexpr int TBL = PAGED ? kDecodeMaxSliceBlocks / 4 : 0;
+  __shared__ __attribute__((aligned(1024))) u32x4 lds[NBUF * TILE_CH + TBL];
+  u32x4(*sk)[TILE_CH] = reinterpret_cast<u32x4(*)[TILE_CH]>(lds);
+  int32_t *s_blk = reinterpret_cast<int32_t *>(lds + NBUF * TILE_CH);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -144,7 +158,10 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
   const int chunk = ((sd.kv_len + D.nsplit - 1) / D.nsplit + BN - 1) / BN * BN;
   const int k_lo = min(sd.kv_len, split * chunk);
   const int k_hi = min(sd.kv_len, k_lo + chunk);
-  const int32_t *kvp = p.kv_pos ? p.kv_pos + sd.kv_begin : nullptr;
+  // paged: kv_pos is indexed by the request's logical rows
+  const int64_t pos_base =
+      PAGED ? (int64_t)sd.req * p.bt_stride * p.block_size + sd.kv_begin : (int64_t)sd.kv_begin;
+  const int32_t *kvp = p.kv_pos ? p.kv_pos + pos_base : nullptr;
   auto key_pos = [&](int j) -> int { return kvp ? kvp[j] : j; };
   // keys past the query's position end the slice early (positions increase)
   int k_vis = k_hi;
@@ -179,8 +196,35 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
   // clamping.  Per-lane byte offsets are relative to the tile's first row.
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)kbase, (short)0, (int)((int64_t)k_hi * p.k_rs * 2), 0x00020000);
+  // paged: the slice's block ids (clamped into the pool) -> LDS
+  const int x_lo = sd.kv_begin + k_lo;  // first logical row of the slice
+  const int blk0 = x_lo / p.block_size;
+  if (PAGED) {
+    if (k_vis > k_lo) {
+      const int nblk = (sd.kv_begin + k_vis - 1) / p.block_size - blk0 + 1;
+      const int32_t *bt = p.block_table + (int64_t)sd.req * p.bt_stride + blk0;
+      for (int i = tid; i < nblk; i += NT) s_blk[i] = min(max(bt[i], 0), p.pool_blocks - 1);
+    }
+    __syncthreads();
+  }
+  auto tile_rsrc = [&](int t, uint32_t &row0) -> __amdgpu_buffer_rsrc_t {
+    if (!PAGED) {
+      row0 = (uint32_t)((k_lo + t * BN) * p.k_rs) * 2u;
+      return krsrc;
+    }
+    // the tile's 32 rows sit in one block; rows past the slice read zero
+    const int x0 = x_lo + t * BN;
+    const int b = __builtin_amdgcn_readfirstlane(s_blk[x0 / p.block_size - blk0]);
+    const int64_t prow = (int64_t)b * p.block_size + x0 % p.block_size;
+    const int rows = min(BN, k_hi - (k_lo + t * BN));
+    row0 = 0u;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const __bf16 *)p.k + prow * p.k_rs + (int64_t)kvh * p.k_hs), (short)0,
+        (int)(rows * p.k_rs * 2), 0x00020000);
+  };
   auto issue = [&](int t) {
-    const uint32_t row0 = (uint32_t)((k_lo + t * BN) * p.k_rs) * 2u;
+    uint32_t row0;
+    const __amdgpu_buffer_rsrc_t trsrc = tile_rsrc(t, row0);
     u32x4 *dst = sk[t % NBUF];
     // recomputed per tile (cheap integer math) instead of kept live in VGPRs
     int ln = lane;
@@ -192,7 +236,7 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
         const int key = slot / KCH, cs = slot % KCH;
         const uint32_t off = (uint32_t)(key * p.k_rs + (cs ^ swz(key)) * 8) * 2u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            krsrc, (__attribute__((address_space(3))) void *)(dst + (wi0 + i) * 64), 16,
+            trsrc, (__attribute__((address_space(3))) void *)(dst + (wi0 + i) * 64), 16,
             row0 + off, 0, 0, 0);
       }
     }
@@ -416,8 +460,12 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const AttnPara
 
 hipError_t launch_attn_decode_mla(const AttnParams &p, const DecodeLaunch &D, hipStream_t stream) {
   if (D.items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_decode_mla_kernel, dim3((unsigned)(D.items * D.nsplit)), dim3(NT), 0,
-                     stream, p, D);
+  if (p.block_table)
+    hipLaunchKernelGGL(attn_decode_mla_kernel<true>, dim3((unsigned)(D.items * D.nsplit)),
+                       dim3(NT), 0, stream, p, D);
+  else
+    hipLaunchKernelGGL(attn_decode_mla_kernel<false>, dim3((unsigned)(D.items * D.nsplit)),
+                       dim3(NT), 0, stream, p, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t waves = (int64_t)D.items * HT;

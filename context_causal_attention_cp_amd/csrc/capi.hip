@@ -52,7 +52,9 @@ cp_status check_attn(const cp_attn_args *a) {
   for (int32_t i = 0; i < a->num_segs; ++i) {
     const cp_segment &s = a->segs[i];
     if (s.q_begin < 0 || s.q_end < s.q_begin || s.q_end > a->num_q_rows) return CP_ERR_ARG;
-    if (s.kv_begin < 0 || s.kv_end < s.kv_begin || s.kv_end > a->num_kv_rows) return CP_ERR_ARG;
+    if (s.kv_begin < 0 || s.kv_end < s.kv_begin) return CP_ERR_ARG;
+    // paged KV: kv ranges count logical rows of the request (checked below)
+    if (!a->block_table && s.kv_end > a->num_kv_rows) return CP_ERR_ARG;
     if (s.pos_stride < 0) return CP_ERR_ARG;
     // every row position must fit int32 with room for the kernels' sentinels
     const int64_t n = s.q_end - s.q_begin;
@@ -68,7 +70,21 @@ cp_status check_attn(const cp_attn_args *a) {
     const int64_t rs = std::max(a->k_row_stride, a->v_row_stride);
     if (64 * rs * 2 > INT32_MAX) return CP_ERR_UNSUPPORTED;
   }
-  if (path == Path::DecodeMla) {
+  if (a->block_table) {
+    // paged KV: the decode shape only; blocks hold whole 32-row tiles
+    if (path != Path::DecodeMla) return CP_ERR_UNSUPPORTED;
+    if (a->block_size < 32 || a->block_size % 32 != 0 || a->block_table_stride < 1)
+      return CP_ERR_ARG;
+    if (a->num_kv_rows < a->block_size) return CP_ERR_ARG;
+    for (int32_t i = 0; i < a->num_segs; ++i) {
+      const cp_segment &g = a->segs[i];
+      if (g.req < 0 || g.kv_begin % 32 != 0 ||
+          g.kv_end > static_cast<int64_t>(a->block_table_stride) * a->block_size)
+        return CP_ERR_ARG;
+    }
+    if (static_cast<int64_t>(a->block_size) * a->k_row_stride * 2 > INT32_MAX) return CP_ERR_UNSUPPORTED;
+  }
+  if (path == Path::DecodeMla && !a->block_table) {
     // the latent rows of a segment are addressed with 32-bit byte offsets
     for (int32_t i = 0; i < a->num_segs; ++i) {
       const int64_t rows = a->segs[i].kv_end - a->segs[i].kv_begin;
@@ -121,6 +137,10 @@ AttnParams make_params(const cp_attn_args &a) {
   p.causal = a.causal ? 1 : 0;
   p.o_bf16 = a.o_dtype == CP_BF16;
   p.accumulate = a.accumulate ? 1 : 0;
+  p.block_table = a.block_table;
+  p.bt_stride = a.block_table_stride;
+  p.block_size = a.block_size;
+  p.pool_blocks = a.block_table && a.block_size > 0 ? a.num_kv_rows / a.block_size : 0;
   p.ws = a.workspace;
   p.ws_bytes = static_cast<int64_t>(a.workspace_bytes);
   return p;
@@ -175,6 +195,7 @@ std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
       d.kv_begin = s.kv_begin;
       d.kv_len = s.kv_end - s.kv_begin;
       d.tile_begin = tiles;
+      d.req = s.req;
       tiles += (d.q_len + tile_rows - 1) / tile_rows;
     }
     L.num_segs = static_cast<int32_t>(n);
@@ -208,6 +229,7 @@ size_t plan_decode(const cp_attn_args &a, std::vector<DecodeLaunch> *out) {
       d.pos_stride = g.pos_stride;
       d.kv_begin = g.kv_begin;
       d.kv_len = g.kv_end - g.kv_begin;
+      d.req = g.req;
       d.tile_begin = items;
       items += d.q_len * a.hkv * htiles;
       min_kv = std::min(min_kv, d.kv_len);
@@ -216,6 +238,13 @@ size_t plan_decode(const cp_attn_args &a, std::vector<DecodeLaunch> *out) {
     const int32_t target = 256;
     int32_t nsplit = std::max<int32_t>(1, (target + items - 1) / items);
     nsplit = std::min<int32_t>(nsplit, std::max<int32_t>(1, min_kv / 256));
+    if (a.block_table) {
+      // a slice's block ids must fit the kernel's LDS table
+      int32_t max_kv = 0;
+      for (size_t j = 0; j < n; ++j) max_kv = std::max(max_kv, D.s[j].kv_len);
+      const int64_t per = static_cast<int64_t>(kDecodeMaxSliceBlocks - 2) * a.block_size;
+      nsplit = std::max<int32_t>(nsplit, static_cast<int32_t>((max_kv + per - 1) / per));
+    }
     D.num_segs = static_cast<int32_t>(n);
     D.items = items;
     D.nsplit = nsplit;

@@ -27,7 +27,7 @@ struct SegDesc {
   int32_t kv_begin;    // first KV row
   int32_t kv_len;      // KV rows visible at most
   int32_t tile_begin;  // first launch tile number of this segment
-  int32_t reserved;
+  int32_t req;         // request index (paged KV: the block-table row)
 };
 
 struct LaunchSegs {
@@ -54,6 +54,10 @@ struct AttnParams {
   int32_t causal;
   int32_t o_bf16;     // 1: o is bf16, 0: fp32
   int32_t accumulate; // 1: merge into the (O, LSE) already in o / lse
+  const int32_t *block_table;  // paged KV, or null
+  int64_t bt_stride;           // entries per request row
+  int32_t block_size;          // rows per block
+  int32_t pool_blocks;         // blocks in the k / v pool
   void *ws;           // workspace (device)
   int64_t ws_bytes;
 };
@@ -65,6 +69,8 @@ struct AttnParams {
 //   ws_o   fp32 [items][nsplit][kDecodeHeadsPerBlock][512]
 //   ws_lse fp32 [items][nsplit][kDecodeHeadsPerBlock]
 constexpr int kDecodeHeadsPerBlock = 128;
+// paged KV: block ids of one key slice staged in LDS
+constexpr int kDecodeMaxSliceBlocks = 1024;
 
 struct DecodeLaunch {
   int32_t num_segs;

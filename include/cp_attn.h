@@ -192,6 +192,19 @@ cp_status cp_ring_pad_len(int32_t cp_size, const int64_t *cached_per_rank, int64
  * A row with no visible key gets o = 0 and lse = -inf.
  * Rows not covered by any segment are not written.
  *
+ * Paged KV (block_table != NULL; the MLA-absorbed decode shape): k and v
+ * address a pool of num_kv_rows rows in blocks of block_size rows, and a
+ * segment's kv range [kv_begin, kv_end) counts logical rows of request
+ * seg.req: logical row x is pool row
+ *   block_table[req * block_table_stride + x / block_size] * block_size
+ *   + x % block_size.
+ * kv_pos (if given) is indexed by logical row, per request:
+ * kv_pos[req * block_table_stride * block_size + x].  Block ids outside the
+ * pool are clamped into it (wrong values, never an out-of-bounds read).
+ * This is how a decode rank stores its shard when the cache is interleaved
+ * over ranks in blocks ("What is Context Parallelism", section 2.2: token
+ * blocks, not single tokens, on shard (i / block) mod W).
+ *
  * accumulate = 1 (the pass-Q running accumulator, same blog section 3.3 and
  * the merge of section 3.6 fused into the epilogue): o and lse already hold
  * a running result (O_acc, L_acc) of the same rows; each row's new partial
@@ -237,6 +250,9 @@ typedef struct {
   void *workspace;         /* device, optional */
   size_t workspace_bytes;
   int32_t accumulate;      /* 0: write (O, LSE); 1: merge into the (O, LSE) in o / lse */
+  const int32_t *block_table;  /* device, optional: paged KV (MLA decode shape only) */
+  int32_t block_table_stride;  /* entries per request row of block_table */
+  int32_t block_size;          /* KV rows per block (a multiple of 32) */
 } cp_attn_args;
 
 /*

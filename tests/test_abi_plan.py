@@ -226,6 +226,39 @@ def test_attn_workspace_required():
     assert _fwd(workspace=FAKE + 4, workspace_bytes=64) == _lib.CP_ERR_ARG   # misaligned
 
 
+def _paged(segs, **kw):
+    # MLA decode shape over a paged pool of 4 blocks of 64 rows
+    arr = (_lib.Segment * len(segs))(*segs)
+    base = dict(hq=128, hkv=1, dqk=576, dv=512, num_q_rows=2, num_kv_rows=256,
+                q_row_stride=128 * 576, q_head_stride=576, k_row_stride=576, k_head_stride=576,
+                v_row_stride=576, v_head_stride=576, o_row_stride=128 * 512, o_head_stride=512,
+                lse_row_stride=128, block_table=FAKE, block_table_stride=8, block_size=64,
+                segs=arr, num_segs=len(segs))
+    base.update(kw)
+    return base
+
+
+def test_paged_kv_arg_errors():
+    S = _lib.Segment
+    ok = [S(0, 0, 1, 600, 1, 0, 512), S(1, 1, 2, 100, 1, 64, 96)]
+    # logical rows may exceed the pool (512 > 256 rows): only the workspace query
+    st, n = _ws(**_paged(ok))
+    assert st == _lib.CP_OK and n > 0
+    bad = [
+        (_paged(ok, block_size=48), _lib.CP_ERR_ARG),        # not a multiple of 32
+        (_paged(ok, block_size=0), _lib.CP_ERR_ARG),
+        (_paged(ok, block_table_stride=0), _lib.CP_ERR_ARG),
+        (_paged(ok, num_kv_rows=32), _lib.CP_ERR_ARG),       # pool smaller than a block
+        (_paged([S(0, 0, 1, 600, 1, 16, 512)]), _lib.CP_ERR_ARG),   # kv_begin off a tile
+        (_paged([S(0, 0, 1, 600, 1, 0, 513)]), _lib.CP_ERR_ARG),    # past the request's table
+        (_paged([S(-1, 0, 1, 600, 1, 0, 64)]), _lib.CP_ERR_ARG),    # no table row
+        (dict(block_table=FAKE, block_table_stride=8, block_size=64), _lib.CP_ERR_UNSUPPORTED),
+    ]
+    for kw, want in bad:
+        assert _ws(**kw)[0] == want, kw
+        assert _fwd(**kw) == want, kw
+
+
 def test_merge_arg_errors():
     L = _lib._lib
     def m(parts=2, rows=4, heads=2, dv=128, op=FAKE, pdt=1, ops=1024, lp=FAKE, lps=8,

@@ -25,7 +25,8 @@ The five workloads follow the shapes the pages use for this problem:
 Tensors are drawn as fp32 N(0, 1) from a seeded ``torch.Generator`` in the
 order Q, K, V, then rounded to bf16 (round-to-nearest-even) where the
 workload says bf16.  Integer draws use ``numpy.random.default_rng(seed)``
-with inclusive bounds.
+with inclusive bounds.  ``paged_layout`` draws a random page allocation
+(a permutation of pool blocks) for the paged-KV decode layout.
 """
 from __future__ import annotations
 
@@ -42,6 +43,7 @@ __all__ = [
     "small",
     "prefill_tensors",
     "decode_tensors",
+    "paged_layout",
     "rand_tensor",
 ]
 
@@ -200,3 +202,27 @@ def decode_tensors(w: Workload, device="cpu", num_reqs: Optional[int] = None,
     q = _randn_chunked((b, w.hq, w.dqk), gen, device, w.dtype)
     kv = _randn_chunked((b * ctx, w.dqk), gen, device, w.dtype).view(b, ctx, w.dqk)
     return q, kv
+
+
+def paged_layout(rows_per_req: Sequence[int], block_size: int, spare_blocks: int, seed: int):
+    """A random page allocation for a paged KV cache: request b's logical
+    rows [0, rows_per_req[b]) are cut into blocks of ``block_size`` rows and
+    every block gets a distinct pool block, drawn as a random permutation of
+    ``sum(blocks) + spare_blocks`` pool blocks (the spare ones stay unused).
+
+    Returns (block_table int32 [B, max blocks] (unused entries -1),
+    pool_row int64 [B, max blocks * block_size] (pool row of every logical
+    row, -1 past the request's end), pool_blocks)."""
+    nblk = [(int(n) + block_size - 1) // block_size for n in rows_per_req]
+    total = sum(nblk) + int(spare_blocks)
+    perm = np.random.default_rng(seed).permutation(total).astype(np.int32)
+    stride = max(1, max(nblk, default=1))
+    table = np.full((len(nblk), stride), -1, dtype=np.int32)
+    pool_row = np.full((len(nblk), stride * block_size), -1, dtype=np.int64)
+    at = 0
+    for b, (n, nb) in enumerate(zip(rows_per_req, nblk)):
+        table[b, :nb] = perm[at:at + nb]
+        at += nb
+        x = np.arange(int(n))
+        pool_row[b, :n] = table[b, x // block_size].astype(np.int64) * block_size + x % block_size
+    return table, pool_row, total
