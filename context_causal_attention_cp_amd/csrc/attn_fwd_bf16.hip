@@ -9,10 +9,11 @@
 // Query head h reads KV head h / (hq/hkv) (GQA, blog section 4.1).
 //
 // One workgroup = 4 waves = 256 query rows of one segment and one head; each
-// wave owns 64 rows (two 32-row MFMA column blocks), one wave per SIMD:
-//   * K and V tiles of 64 keys are copied HBM -> LDS by range-checked buffer
-//     loads straight into XOR-swizzled tiles (no register staging), three
-//     stages in flight;
+// wave owns 64 rows (two 32-row MFMA column blocks), one wave per SIMD (128
+// rows and one block per wave for calls too small to fill the chip otherwise):
+//   * K and V tiles of 32 keys are copied HBM -> LDS by range-checked buffer
+//     loads straight into LDS (no register staging), in keys-fastest layouts
+//     that need no swizzle; up to eight stages, five or six tiles in flight;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, query rows = N): each
 //     lane holds scores of one query row, so the softmax is lane-local; the
 //     Q fragments stay in registers; every K fragment read from LDS feeds two
@@ -20,13 +21,17 @@
 //   * O^T += V^T P^T: P leaves the score registers as the B operand; V^T is
 //     read from the row-major V tile with the transposing LDS read
 //     ds_read_b64_tr_b16, in the accumulator's key order;
-//   * exp2 with scale*log2(e) folded into one FMA; the reference max of a row
-//     only moves (with an accumulator rescale) when the row outgrows it by
-//     more than 2^8;
+//   * the loop is software-pipelined: the products of tile t + 1 run on the
+//     matrix cores while the exponentials of tile t run on the VALU;
+//   * exp2 with scale*log2(e) folded into one FMA; each row's reference max
+//     is fixed from its first tile (main pass), and a workgroup whose scores
+//     outgrow it by more than 2^64 is flagged and recomputed by an exact pass
+//     that moves the reference (with an accumulator rescale) instead;
 //   * per wave, the number of visible tiles and of fully visible tiles is
 //     counted once up front from the tiles' first/last key positions (one
 //     wave-wide vector load per 64 tiles); only boundary tiles are masked;
-//   * O is transposed through LDS and written as whole rows.
+//   * O is transposed through LDS and written as whole rows (or merged into
+//     a running (O, LSE) in accumulate mode).
 // Work mapping: all workgroups of one KV head go to one XCD (id mod 8) so the
 // ones streaming the same K/V share that XCD's L2; inside a head the
 // heaviest tiles (longest causal extent) start first.
