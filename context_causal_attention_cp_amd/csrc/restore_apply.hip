@@ -7,7 +7,8 @@
 // index (restore[g] = slot of flattened new token g) yields causal order.
 // dst row i = src row index[i].
 //
-// HBM-bound copy.  A workgroup pass covers 256 / L rows with L lanes per
+// HBM-bound copy (loads and stores streamed past the caches; a lane keeps
+// eight 16-byte chunks in flight).  A workgroup pass covers 256 / L rows with L lanes per
 // row (L = the power of two nearest above the row's 16-byte chunk count,
 // capped at 256), so short rows do not leave lanes idle and long rows are
 // streamed by the whole workgroup.  Rows whose index is out of range are
@@ -46,16 +47,23 @@ __global__ __launch_bounds__(NT) void restore_apply_kernel(const int32_t *__rest
       continue;
     }
     const u32x4 *sp = (const u32x4 *)(src + s * src_stride);
-    // four chunks in flight per lane
+    // eight, then four chunks in flight per lane; streamed (not kept in cache)
     int c = sub;
-    for (; c + 3 * lanes < cpr; c += 4 * lanes) {
-      const u32x4 a = sp[c], b = sp[c + lanes], e = sp[c + 2 * lanes], f = sp[c + 3 * lanes];
-      d[c] = a;
-      d[c + lanes] = b;
-      d[c + 2 * lanes] = e;
-      d[c + 3 * lanes] = f;
+    for (; c + 7 * lanes < cpr; c += 8 * lanes) {
+      u32x4 x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = __builtin_nontemporal_load(sp + c + j * lanes);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) __builtin_nontemporal_store(x[j], d + c + j * lanes);
     }
-    for (; c < cpr; c += lanes) d[c] = sp[c];
+    for (; c + 3 * lanes < cpr; c += 4 * lanes) {
+      u32x4 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = __builtin_nontemporal_load(sp + c + j * lanes);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(x[j], d + c + j * lanes);
+    }
+    for (; c < cpr; c += lanes) __builtin_nontemporal_store(__builtin_nontemporal_load(sp + c), d + c);
   }
 }
 
