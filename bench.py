@@ -38,6 +38,8 @@ def _args():
     ap.add_argument("--no-extra", action="store_true", help="only the headline step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--only", choices=["decode", "decode_paged", "restore"],
+                    help="only this measurement of the extra section (for profiling)")
     return ap.parse_args()
 
 
@@ -98,6 +100,9 @@ def main():
     import torch
 
     import context_causal_attention_cp_amd as cp
+    if a.only:
+        _only(cp, a.only)
+        return
     import workloads
 
     dev = "cuda"
@@ -229,6 +234,20 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _only(cp, name):
+    """One measurement of the extra section on its own, as a JSON line."""
+    import workloads
+    if name == "decode":
+        out = _decode(cp, workloads.get("decode_mla_b64"))
+    elif name == "decode_paged":
+        out = _decode_paged(cp, workloads.get("decode_mla_b64"), 128)
+    else:
+        w = workloads.get("zigzag_t131072_mla")
+        _, k, _ = workloads.prefill_tensors(w, "cuda")
+        out = _restore(cp, w, k)
+    print(json.dumps({"only": name, **out}), flush=True)
+
+
 def _time_ms(fn, reps=5, warm=1):
     """Average time of ``fn`` (HIP events on the current stream)."""
     import torch
@@ -282,7 +301,8 @@ def _restore(cp, w, k):
     del dst
     torch.cuda.empty_cache()
     return {"ms": round(ms, 4), "algorithmic_bytes": by, "GB/s": round(by / ms / 1e6, 1),
-            "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4)}
+            "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "traffic": _profiled_traffic("restore_apply_kernel", "restore_apply.hip")}
 
 
 def _direct(cp, w, q_loc, k, v, plan):
@@ -410,7 +430,8 @@ def _decode_paged(cp, w, bs):
             "contiguous_ms": round(cont, 4), "algorithmic_bytes": by,
             "paged_GB/s": round(by / paged / 1e6, 1),
             "paged_frac_hbm": round(by / paged / 1e6 / PEAK_HBM_GBS, 4),
-            "paged_over_contiguous": round(paged / cont, 4)}
+            "paged_over_contiguous": round(paged / cont, 4),
+            "traffic_contiguous": _profiled_traffic("attn_decode_mla_kernel", "attn_decode_mla.hip")}
 
 
 def _cpu_baseline(w, q, k, v, plan, budget_s):
