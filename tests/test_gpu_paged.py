@@ -151,3 +151,53 @@ def test_paged_decode_mla_b64_block128():
             compare(f64(o[b]), f64(l[b]), ro, rl, range(w.hq), "bf16", f"rank {j} req {b}")
         del pg
         torch.cuda.empty_cache()
+
+
+def test_paged_gqa_empty_and_invisible():
+    """Two latent KV heads (64 query heads each) in one paged pool, an empty
+    segment, and a query that sits before every key of the rank: the empty
+    and the invisible rows get O = 0, LSE = -inf; the others match the
+    oracle and the same call on contiguous rows bit for bit."""
+    B, ctx, W, j, bs, hq, hkv = 3, 1200, 2, 1, 64, 128, 2
+    g = torch.Generator(device=DEV)
+    g.manual_seed(99)
+    q = torch.randn((B, hq, DQK), generator=g, device=DEV).to(torch.bfloat16)
+    kv = torch.randn((B, ctx, hkv, DQK), generator=g, device=DEV).to(torch.bfloat16)
+    scale = 1.0 / np.sqrt(DQK)
+    keys = _rank_keys(ctx, W, j, bs)          # rank 1 of 2: blocks 1, 3, 5, ...
+    n = len(keys)
+    table, pool_row, nblocks = workloads.paged_layout([n] * B, bs, 3, 5)
+    stride = table.shape[1]
+    pool = torch.full((nblocks * bs, hkv, DQK), float("nan"), device=DEV, dtype=kv.dtype)
+    src = torch.from_numpy((np.arange(B)[:, None] * ctx + keys[None, :]).reshape(-1)).to(DEV)
+    flat = kv.reshape(B * ctx, hkv, DQK)
+    pool[torch.from_numpy(pool_row[:, :n].reshape(-1)).to(DEV)] = flat[src]
+    pos = np.full((B, stride * bs), 1 << 30, dtype=np.int32)
+    pos[:, :n] = keys
+    pos_t = torch.from_numpy(pos.reshape(-1)).to(DEV)
+    # request 0: whole shard; request 1: empty range; request 2: query at
+    # position 10, before the rank's first key (64)
+    q_pos = [ctx, ctx, 10]
+    segs = [cp.Segment(0, 0, 1, q_pos[0], 1, 0, n), cp.Segment(1, 1, 2, q_pos[1], 1, 64, 64),
+            cp.Segment(2, 2, 3, q_pos[2], 1, 0, n)]
+    say("paged decode GQA 2 KV heads, empty and invisible rows")
+    o, l = cp.attn_fwd(q, pool, pool[:, :, :DV], segs, scale, kv_pos=pos_t, o_dtype=torch.float32,
+                       block_table=torch.from_numpy(table).to(DEV), block_size=bs)
+    kc = flat[src].view(B * n, hkv, DQK)
+    segs_c = [cp.Segment(0, 0, 1, q_pos[0], 1, 0, n), cp.Segment(1, 1, 2, q_pos[1], 1, n + 64, n + 64),
+              cp.Segment(2, 2, 3, q_pos[2], 1, 2 * n, 3 * n)]
+    oc, lc = cp.attn_fwd(q, kc, kc[:, :, :DV], segs_c, scale,
+                         kv_pos=torch.from_numpy(np.tile(keys, B).astype(np.int32)).to(DEV),
+                         o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc) and torch.equal(l, lc)
+    q64, kv64 = f64(q), f64(kv)
+    G = hq // hkv
+    for kvh in range(hkv):
+        hs = slice(kvh * G, (kvh + 1) * G)
+        ro, rl = ao.attend(q64[0, hs], kv64[0, keys, kvh], kv64[0, keys, kvh, :DV], [ctx] * G, keys,
+                           scale)
+        compare(f64(o[0, hs]), f64(l[0, hs]), ro, rl, range(G), "bf16", f"req 0 kv head {kvh}")
+    for b in (1, 2):
+        lb = f64(l[b])
+        assert np.all(lb == -np.inf) and np.all(f64(o[b]) == 0), f"req {b}: not empty"
