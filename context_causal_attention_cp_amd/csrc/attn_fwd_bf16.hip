@@ -131,15 +131,15 @@ __device__ inline void wait_later(int later) {
 }
 
 // Accumulate mode: merge a row's new normalised partial (8 elements a, c at
-// dv offset d0, log-sum-exp ln) into the running (O, LSE) of that row in
-// p.o / p.lse, in place: m = max(la, ln), w = exp(l - m),
+// dv offset d0, log-sum-exp ln) into the running (O, LSE) of output row orow
+// in p.o / p.lse, in place: m = max(la, ln), w = exp(l - m),
 // O = (wa Oa + wn On) / (wa + wn), L = m + ln(wa + wn).  la = -inf means an
 // empty accumulator (Oa not read).  Returns false if ln = -inf (nothing to
 // merge: the row is left as it is).  The lane with write_lse stores L.
-__device__ inline bool merge_into(const AttnParams &p, int64_t qrow, int h, int d0, float ln,
+__device__ inline bool merge_into(const AttnParams &p, int64_t orow, int h, int d0, float ln,
                                   bool write_lse, float4 &a, float4 &c) {
   if (ln == -INFINITY) return false;
-  float *lp = p.lse + qrow * p.lse_rs + h;
+  float *lp = p.lse + orow * p.lse_rs + h;
   const float la = *lp;
   float lnew = ln;
   if (la != -INFINITY) {
@@ -148,14 +148,14 @@ __device__ inline bool merge_into(const AttnParams &p, int64_t qrow, int h, int 
     const float inv = 1.f / (wa + wn);
     float oa[8];
     if (p.o_bf16) {
-      const u32x4 v = *(const u32x4 *)((const __bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + d0);
+      const u32x4 v = *(const u32x4 *)((const __bf16 *)p.o + orow * p.o_rs + (int64_t)h * p.o_hs + d0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         oa[2 * i] = __uint_as_float(v[i] << 16);
         oa[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
       }
     } else {
-      const float *op = (const float *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + d0;
+      const float *op = (const float *)p.o + orow * p.o_rs + (int64_t)h * p.o_hs + d0;
       const float4 x = *(const float4 *)op, y = *(const float4 *)(op + 4);
       oa[0] = x.x; oa[1] = x.y; oa[2] = x.z; oa[3] = x.w;
       oa[4] = y.x; oa[5] = y.y; oa[6] = y.z; oa[7] = y.w;
@@ -595,8 +595,8 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
       }
     if (hf == 0) s_lse[w * 32 + n] = lse[rb];
     if (!p.accumulate && hf == 0 && valid[rb]) {
-      const int64_t qrow = (int64_t)sd.q_begin + row0 + w * RW + rb * 32 + n;
-      p.lse[qrow * p.lse_rs + h] = lse[rb];
+      const int64_t orow = (int64_t)sd.o_begin + row0 + w * RW + rb * 32 + n;
+      p.lse[orow * p.lse_rs + h] = lse[rb];
     }
     __builtin_amdgcn_s_barrier();  // (wave-local data; keeps the waves in step)
     // whole rows: 8 output elements per lane
@@ -610,8 +610,8 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
       if (rr < rows_here) {
         float4 a = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ);
         float4 c = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ + 16);
-        const int64_t qrow = (int64_t)sd.q_begin + row0 + rr;
-        if (p.accumulate && !merge_into(p, qrow, h, sub * 8, s_lse[w * 32 + r], sub == 0, a, c))
+        const int64_t orow = (int64_t)sd.o_begin + row0 + rr;
+        if (p.accumulate && !merge_into(p, orow, h, sub * 8, s_lse[w * 32 + r], sub == 0, a, c))
           continue;  // no visible key in this call: the accumulator row stays
         if (p.o_bf16) {
           u32x4 v;
@@ -619,9 +619,9 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
           v[1] = pack_bf16(a.z, a.w);
           v[2] = pack_bf16(c.x, c.y);
           v[3] = pack_bf16(c.z, c.w);
-          *(u32x4 *)((__bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + sub * 8) = v;
+          *(u32x4 *)((__bf16 *)p.o + orow * p.o_rs + (int64_t)h * p.o_hs + sub * 8) = v;
         } else {
-          float *op = (float *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs + sub * 8;
+          float *op = (float *)p.o + orow * p.o_rs + (int64_t)h * p.o_hs + sub * 8;
           *(float4 *)op = a;
           *(float4 *)(op + 4) = c;
         }

@@ -47,6 +47,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const AttnParams p, co
 
   const bool valid = lane < rows_here;
   const int64_t qrow = (int64_t)sd.q_begin + row0 + lane;
+  const int64_t orow = (int64_t)sd.o_begin + row0 + lane;  // output row
   const int qpos = valid ? sd.pos_begin + (row0 + lane) * sd.pos_stride : kNoPos;
   const int qmax = sd.pos_begin + (row0 + rows_here - 1) * sd.pos_stride;
 
@@ -104,28 +105,28 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const AttnParams p, co
     // merge into the running (O, LSE) of this row: an empty new partial
     // leaves it; an empty accumulator (LSE = -inf) is replaced
     if (!any) return;
-    const float la = p.lse[qrow * p.lse_rs + h];
+    const float la = p.lse[orow * p.lse_rs + h];
     if (la != -INFINITY) {
       const float mm = fmaxf(la, lse);
       const float wa = expf(la - mm), wn = expf(lse - mm);
       const float winv = 1.f / (wa + wn);
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        const float oa = p.o_bf16 ? (float)((const __bf16 *)p.o)[qrow * p.o_rs + (int64_t)h * p.o_hs + d]
-                                  : ((const float *)p.o)[qrow * p.o_rs + (int64_t)h * p.o_hs + d];
+        const float oa = p.o_bf16 ? (float)((const __bf16 *)p.o)[orow * p.o_rs + (int64_t)h * p.o_hs + d]
+                                  : ((const float *)p.o)[orow * p.o_rs + (int64_t)h * p.o_hs + d];
         o[d] = (wa * oa + wn * o[d] * inv) * winv;
       }
       inv = 1.f;
       lse = mm + logf(wa + wn);
     }
   }
-  p.lse[qrow * p.lse_rs + h] = lse;
+  p.lse[orow * p.lse_rs + h] = lse;
   if (p.o_bf16) {
-    __bf16 *op = (__bf16 *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs;
+    __bf16 *op = (__bf16 *)p.o + orow * p.o_rs + (int64_t)h * p.o_hs;
 #pragma unroll
     for (int d = 0; d < D; ++d) op[d] = (__bf16)(o[d] * inv);
   } else {
-    float *op = (float *)p.o + qrow * p.o_rs + (int64_t)h * p.o_hs;
+    float *op = (float *)p.o + orow * p.o_rs + (int64_t)h * p.o_hs;
 #pragma unroll
     for (int d = 0; d < D; ++d) op[d] = o[d] * inv;
   }

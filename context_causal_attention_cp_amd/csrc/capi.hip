@@ -146,39 +146,28 @@ AttnParams make_params(const cp_attn_args &a) {
   return p;
 }
 
-// Below this many 256-row workgroups a bf16 call uses 128-row workgroups
-// (two per compute unit of the 256).
-constexpr int64_t kSmallGridWorkgroups = 512;
+// One segment as a launch sees it: the caller's segment, or one key chunk of
+// it (split calls), with the row its outputs go to.
+struct PlanSeg {
+  cp_segment g;
+  int32_t o_begin;
+};
 
-// Rows per workgroup of a bf16 call: 256, or 128 when the 256-row tiles
-// would give fewer than kSmallGridWorkgroups workgroups.
-int bf16_tile_rows(const cp_attn_args &a) {
-  const int big = attn_bf16_tile_rows(a.dqk, a.dv, false);
-  int64_t wgs = 0;
-  for (int32_t i = 0; i < a.num_segs; ++i)
-    if (a.segs[i].kv_end > a.segs[i].kv_begin)
-      wgs += static_cast<int64_t>((a.segs[i].q_end - a.segs[i].q_begin + big - 1) / big) * a.hq;
-  return attn_bf16_tile_rows(a.dqk, a.dv, wgs < kSmallGridWorkgroups);
+std::vector<PlanSeg> plain_segs(const cp_attn_args &a) {
+  std::vector<PlanSeg> v;
+  for (int32_t i = 0; i < a.num_segs; ++i) v.push_back({a.segs[i], a.segs[i].q_begin});
+  return v;
 }
 
 // Splits the non-empty segments into launches of at most kMaxLaunchSegs,
 // heaviest first (largest visible KV extent), numbering their tiles.
-std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows);
-
-// bf16 workspace: one int32 flag per workgroup of every launch, 16-byte rounded
-size_t bf16_flag_bytes(const cp_attn_args &a, const std::vector<LaunchSegs> &launches) {
-  int64_t wgs = 0;
-  for (const LaunchSegs &L : launches) wgs += static_cast<int64_t>(L.num_tiles) * a.hq;
-  return static_cast<size_t>((wgs * 4 + 15) / 16 * 16);
-}
-
-std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
+std::vector<LaunchSegs> plan_launches(const std::vector<PlanSeg> &segs, int tile_rows) {
   std::vector<int32_t> order;
-  for (int32_t i = 0; i < a.num_segs; ++i)
-    if (a.segs[i].q_end > a.segs[i].q_begin && a.segs[i].kv_end > a.segs[i].kv_begin)
-      order.push_back(i);
+  for (size_t i = 0; i < segs.size(); ++i)
+    if (segs[i].g.q_end > segs[i].g.q_begin && segs[i].g.kv_end > segs[i].g.kv_begin)
+      order.push_back(static_cast<int32_t>(i));
   std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-    return a.segs[x].kv_end - a.segs[x].kv_begin > a.segs[y].kv_end - a.segs[y].kv_begin;
+    return segs[x].g.kv_end - segs[x].g.kv_begin > segs[y].g.kv_end - segs[y].g.kv_begin;
   });
   std::vector<LaunchSegs> out;
   for (size_t i = 0; i < order.size(); i += kMaxLaunchSegs) {
@@ -186,7 +175,8 @@ std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
     const size_t n = std::min<size_t>(kMaxLaunchSegs, order.size() - i);
     int32_t tiles = 0;
     for (size_t j = 0; j < n; ++j) {
-      const cp_segment &s = a.segs[order[i + j]];
+      const PlanSeg &ps = segs[order[i + j]];
+      const cp_segment &s = ps.g;
       SegDesc &d = L.s[j];
       d.q_begin = s.q_begin;
       d.q_len = s.q_end - s.q_begin;
@@ -196,6 +186,7 @@ std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
       d.kv_len = s.kv_end - s.kv_begin;
       d.tile_begin = tiles;
       d.req = s.req;
+      d.o_begin = ps.o_begin;
       tiles += (d.q_len + tile_rows - 1) / tile_rows;
     }
     L.num_segs = static_cast<int32_t>(n);
@@ -205,9 +196,106 @@ std::vector<LaunchSegs> plan_launches(const cp_attn_args &a, int tile_rows) {
   return out;
 }
 
-// Decode launches: segments in chunks of kMaxLaunchSegs; the key range of
-// each (row, KV head, head block) is cut into nsplit slices so that the grid
-// covers the chip.  Returns the workspace bytes the largest launch needs.
+// Below this many workgroups a bf16 call is too small to fill the 256
+// compute units well.
+constexpr int64_t kSmallGridWorkgroups = 512;
+// Split calls: aim for this many workgroups, with key chunks of at least
+// kMinSplitKeys keys and at most kMaxSplitParts chunks per segment.
+constexpr int64_t kSplitTargetWorkgroups = 1024;
+constexpr int64_t kMinSplitKeys = 1024;
+constexpr int32_t kMaxSplitParts = 16;
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The bf16 launch plan.  A call whose segments give fewer than
+// kSmallGridWorkgroups 128-row workgroups has its long key ranges cut into
+// chunks: every chunk of a segment is a launch segment of its own (same
+// query rows, positions shifted with the chunk when they are implicit) that
+// writes a normalised partial (O_s, LSE_s) to the workspace, and the parts
+// of each segment are merged by log-sum-exp into the caller's rows
+// ("What is Context Parallelism" blog, section 3.6: the merge is exact for
+// any partition of the keys).  Otherwise: 256-row workgroups, or 128-row
+// ones below kSmallGridWorkgroups, writing O and LSE directly.
+struct Bf16Plan {
+  int tile_rows = 0;
+  int32_t parts = 0;               // > 0: split; parts per segment in seg_parts
+  std::vector<int32_t> seg_parts;  // per caller segment
+  std::vector<LaunchSegs> launches;
+  size_t flag_bytes = 0, part_o_bytes = 0, part_lse_bytes = 0;
+  size_t bytes() const { return flag_bytes + part_o_bytes + part_lse_bytes; }
+};
+
+Bf16Plan plan_bf16(const cp_attn_args &a) {
+  Bf16Plan P;
+  const int small = attn_bf16_tile_rows(a.dqk, a.dv, true);
+  const int big = attn_bf16_tile_rows(a.dqk, a.dv, false);
+  int64_t wgs_small = 0, wgs_big = 0, work = 0, max_kv = 0;
+  for (int32_t i = 0; i < a.num_segs; ++i) {
+    const cp_segment &g = a.segs[i];
+    const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
+    if (nq <= 0 || nk <= 0) continue;
+    wgs_small += (nq + small - 1) / small * a.hq;
+    wgs_big += (nq + big - 1) / big * a.hq;
+    work += (nq + big - 1) / big * a.hq * nk;
+    max_kv = std::max(max_kv, nk);
+  }
+  // the merge writes whole (row, head) runs: dense O and LSE rows only
+  const bool dense = a.o_head_stride == a.dv &&
+                     a.o_row_stride == static_cast<int64_t>(a.hq) * a.dv &&
+                     a.lse_row_stride == a.hq;
+  const bool can_split = !a.accumulate && !a.block_table && dense &&
+                         wgs_small < kSmallGridWorkgroups && max_kv <= (1 << 28);
+  std::vector<PlanSeg> segs;
+  if (can_split) {
+    int64_t chunk = std::max<int64_t>(kMinSplitKeys, (work + kSplitTargetWorkgroups - 1) /
+                                                         kSplitTargetWorkgroups);
+    chunk = (chunk + 31) / 32 * 32;
+    P.seg_parts.assign(a.num_segs, 0);
+    for (int32_t i = 0; i < a.num_segs; ++i) {
+      const cp_segment &g = a.segs[i];
+      const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
+      if (nq <= 0 || nk <= 0) continue;
+      const int64_t np = std::min<int64_t>(kMaxSplitParts, (nk + chunk - 1) / chunk);
+      const int64_t c = ((nk + np - 1) / np + 31) / 32 * 32;  // whole tiles per chunk
+      int32_t made = 0;
+      for (int64_t off = 0; off < nk; off += c, ++made) {
+        PlanSeg ps{g, 0};
+        ps.g.kv_begin = static_cast<int32_t>(g.kv_begin + off);
+        ps.g.kv_end = static_cast<int32_t>(std::min<int64_t>(g.kv_end, g.kv_begin + off + c));
+        // implicit key positions count from the chunk start: shift the rows'
+        // positions with it (kv_pos gives absolute positions)
+        if (!a.kv_pos) ps.g.pos_begin = static_cast<int32_t>(g.pos_begin - off);
+        ps.o_begin = made * a.num_q_rows + g.q_begin;
+        segs.push_back(ps);
+      }
+      P.seg_parts[i] = made;
+      P.parts = std::max(P.parts, made);
+    }
+    if (P.parts <= 1) {  // nothing long enough to split
+      P.parts = 0;
+      P.seg_parts.clear();
+      segs.clear();
+    }
+  }
+  if (P.parts > 0) {
+    P.tile_rows = big;
+    const size_t elt = a.o_dtype == CP_BF16 ? 2 : 4;
+    P.part_o_bytes = round256(static_cast<size_t>(P.parts) * a.num_q_rows * a.hq * a.dv * elt);
+    P.part_lse_bytes = round256(static_cast<size_t>(P.parts) * a.num_q_rows * a.hq * 4);
+  } else {
+    P.tile_rows = wgs_big < kSmallGridWorkgroups ? small : big;
+    segs = plain_segs(a);
+  }
+  P.launches = plan_launches(segs, P.tile_rows);
+  int64_t wgs = 0;
+  for (const LaunchSegs &L : P.launches) wgs += static_cast<int64_t>(L.num_tiles) * a.hq;
+  // one int32 flag per workgroup of every launch (16-byte rounded; the
+  // partials that follow start on a 256-byte boundary)
+  P.flag_bytes = (static_cast<size_t>(wgs) * 4 + 15) / 16 * 16;
+  if (P.parts > 0) P.flag_bytes = round256(P.flag_bytes);
+  return P;
+}
+
 size_t plan_decode(const cp_attn_args &a, std::vector<DecodeLaunch> *out) {
   const int G = a.hq / a.hkv;
   const int htiles = (G + kDecodeHeadsPerBlock - 1) / kDecodeHeadsPerBlock;
@@ -329,7 +417,7 @@ extern "C" cp_status cp_attn_workspace_size(const cp_attn_args *a, size_t *bytes
   *bytes = 0;
   const Path path = pick_path(*a);
   if (path == Path::DecodeMla) *bytes = plan_decode(*a, nullptr);
-  if (path == Path::Bf16Mfma) *bytes = bf16_flag_bytes(*a, plan_launches(*a, bf16_tile_rows(*a)));
+  if (path == Path::Bf16Mfma) *bytes = plan_bf16(*a).bytes();
   return CP_OK;
 }
 
@@ -356,25 +444,48 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
     return fill_empty_segments(a, s);
   }
   if (path == Path::F32) {
-    for (const LaunchSegs &L : plan_launches(*a, attn_f32_tile_rows(a->dqk))) {
+    for (const LaunchSegs &L : plan_launches(plain_segs(*a), attn_f32_tile_rows(a->dqk))) {
       const hipError_t e = launch_attn_f32(p, L, a->dqk, s);
       if (e != hipSuccess) return device_error(e);
     }
     return fill_empty_segments(a, s);
   }
-  // bf16: each launch's workgroups get one int32 flag in the workspace
-  const int tile_rows = bf16_tile_rows(*a);
-  const std::vector<LaunchSegs> launches = plan_launches(*a, tile_rows);
-  const size_t need = bf16_flag_bytes(*a, launches);
+  // bf16: one int32 flag per workgroup, then (split calls) the partials
+  const Bf16Plan P = plan_bf16(*a);
+  const size_t need = P.bytes();
   if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return CP_ERR_SMALL_BUFFER;
   if (need > 0 && !aligned16(a->workspace)) return CP_ERR_ARG;
+  char *ws = static_cast<char *>(a->workspace);
   AttnParams q = p;
-  int32_t *flags = static_cast<int32_t *>(a->workspace);
-  for (const LaunchSegs &L : launches) {
+  const int o_bf16 = a->o_dtype == CP_BF16 ? 1 : 0;
+  const int64_t part_rows = static_cast<int64_t>(a->num_q_rows) * a->hq;  // (row, head) per part
+  if (P.parts > 0) {
+    // partial j of a segment's rows: rows j * num_q_rows + [q_begin, q_end)
+    q.o = ws + P.flag_bytes;
+    q.o_rs = static_cast<int64_t>(a->hq) * a->dv;
+    q.o_hs = a->dv;
+    q.lse = reinterpret_cast<float *>(ws + P.flag_bytes + P.part_o_bytes);
+    q.lse_rs = a->hq;
+  }
+  int32_t *flags = reinterpret_cast<int32_t *>(ws);
+  for (const LaunchSegs &L : P.launches) {
     q.ws = flags;
-    const hipError_t e = launch_attn_bf16(q, L, a->dqk, a->dv, tile_rows, s);
+    const hipError_t e = launch_attn_bf16(q, L, a->dqk, a->dv, P.tile_rows, s);
     if (e != hipSuccess) return device_error(e);
     flags += static_cast<int64_t>(L.num_tiles) * a->hq;
+  }
+  for (int32_t i = 0; i < a->num_segs && P.parts > 0; ++i) {
+    const cp_segment &g = a->segs[i];
+    const int32_t np = P.seg_parts[i];
+    if (np == 0) continue;
+    const int64_t off = static_cast<int64_t>(g.q_begin) * a->hq;  // first (row, head) pair
+    const size_t elt = o_bf16 ? 2 : 4;
+    const hipError_t e = launch_lse_merge(
+        np, static_cast<int64_t>(g.q_end - g.q_begin) * a->hq, a->dv,
+        static_cast<const char *>(q.o) + off * a->dv * elt, o_bf16, part_rows * a->dv,
+        q.lse + off, part_rows, static_cast<char *>(a->o) + off * a->dv * elt, o_bf16,
+        a->lse + off, s);
+    if (e != hipSuccess) return device_error(e);
   }
   return fill_empty_segments(a, s);
 }

@@ -28,6 +28,8 @@ struct SegDesc {
   int32_t kv_len;      // KV rows visible at most
   int32_t tile_begin;  // first launch tile number of this segment
   int32_t req;         // request index (paged KV: the block-table row)
+  int32_t o_begin;     // output row (O, LSE) of the first row (q_begin unless split)
+  int32_t reserved;
 };
 
 struct LaunchSegs {

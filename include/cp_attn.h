@@ -260,9 +260,14 @@ typedef struct {
  * these arguments.  bf16 (dqk, dv) in {(64,64), (128,128), (192,128)}: one
  * int32 per workgroup, i.e. 4 bytes per head per 128 or 256 query rows of
  * each segment (the kernel flags there the rare workgroups whose scores
- * outgrow the softmax reference of their first tile, and recomputes them);
- * the MLA-absorbed decode shape: its split-KV partials; fp32: 0.  Only the
- * shape fields and segs are read.  The contents need no initialisation and
+ * outgrow the softmax reference of their first tile, and recomputes them).
+ * A call too small to fill the GPU (fewer than 512 workgroups of 128 rows;
+ * accumulate = 0, dense o and lse rows, no block table) cuts its long key
+ * ranges into chunks and merges the chunks' partials by log-sum-exp (blog
+ * section 3.6): then the workspace also holds up to 16 partial (O, LSE) per
+ * row and head, in o_dtype.  The MLA-absorbed decode shape: its split-KV
+ * partials; fp32: 0.  Only the shape fields, the strides, accumulate,
+ * block_table and segs are read.  The contents need no initialisation and
  * are scratch after the call.
  * Errors: as cp_attn_fwd's argument checks.
  */

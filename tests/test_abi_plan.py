@@ -219,6 +219,25 @@ def test_workspace_size_query():
     assert _ws(hq=3)[0] == _lib.CP_ERR_ARG
 
 
+def test_split_workspace_size():
+    # one 512-row causal segment against 8192 keys, 32 heads, bf16 out: 4 x 32
+    # 128-row workgroups (< 512), so the keys are cut into 8 chunks of 1024 and
+    # every chunk is a 2 x 32-workgroup launch segment writing a partial:
+    # flags 8 x 64 x 4 B + partial O 8 x 512 x 32 x 128 x 2 B + LSE 8 x 512 x 32 x 4 B
+    segs = (_lib.Segment * 1)(_lib.Segment(0, 0, 512, 7680, 1, 0, 8192))
+    kw = dict(num_q_rows=512, num_kv_rows=8192, hq=32, hkv=8, q_row_stride=32 * 128,
+              k_row_stride=8 * 128, v_row_stride=8 * 128, o_row_stride=32 * 128,
+              lse_row_stride=32, segs=segs, num_segs=1)
+    assert _ws(**kw) == (_lib.CP_OK, 2048 + 8 * 512 * 32 * 128 * 2 + 8 * 512 * 32 * 4)
+    # non-dense output rows: no split, flags of the 4 x 32 128-row workgroups only
+    assert _ws(**dict(kw, o_row_stride=32 * 128 + 8)) == (_lib.CP_OK, 512)
+    # short keys: nothing to split
+    short = (_lib.Segment * 1)(_lib.Segment(0, 0, 512, 0, 1, 0, 1000))
+    assert _ws(**dict(kw, segs=short)) == (_lib.CP_OK, 512)
+    # accumulate mode never splits
+    assert _ws(**dict(kw, accumulate=1)) == (_lib.CP_OK, 512)
+
+
 def test_attn_workspace_required():
     # the bf16 path needs its flag workspace: refused before any launch
     assert _fwd() == _lib.CP_ERR_SMALL_BUFFER
