@@ -220,6 +220,8 @@ struct Bf16Plan {
   int tile_rows = 0;
   int32_t parts = 0;               // > 0: split; parts per segment in seg_parts
   std::vector<int32_t> seg_parts;  // per caller segment
+  std::vector<int32_t> seg_row;    // per caller segment: its first compact partial row
+  int64_t part_rows = 0;           // compact rows per part (rows of the split segments)
   std::vector<LaunchSegs> launches;
   size_t flag_bytes = 0, part_o_bytes = 0, part_lse_bytes = 0;
   size_t bytes() const { return flag_bytes + part_o_bytes + part_lse_bytes; }
@@ -243,6 +245,8 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
   const bool dense = a.o_head_stride == a.dv &&
                      a.o_row_stride == static_cast<int64_t>(a.hq) * a.dv &&
                      a.lse_row_stride == a.hq;
+  // (fewer than kSmallGridWorkgroups 128-row workgroups also bounds the rows:
+  // kMaxSplitParts x rows stays far inside int32)
   const bool can_split = !a.accumulate && !a.block_table && dense &&
                          wgs_small < kSmallGridWorkgroups && max_kv <= (1 << 28);
   std::vector<PlanSeg> segs;
@@ -251,6 +255,16 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
                                                          kSplitTargetWorkgroups);
     chunk = (chunk + 31) / 32 * 32;
     P.seg_parts.assign(a.num_segs, 0);
+    P.seg_row.assign(a.num_segs, 0);
+    // partial rows are compact: the rows of the split segments, numbered in
+    // segment order, one block of them per part
+    for (int32_t i = 0; i < a.num_segs; ++i) {
+      const cp_segment &g = a.segs[i];
+      if (g.q_end > g.q_begin && g.kv_end > g.kv_begin) {
+        P.seg_row[i] = static_cast<int32_t>(P.part_rows);
+        P.part_rows += g.q_end - g.q_begin;
+      }
+    }
     for (int32_t i = 0; i < a.num_segs; ++i) {
       const cp_segment &g = a.segs[i];
       const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
@@ -265,7 +279,7 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
         // implicit key positions count from the chunk start: shift the rows'
         // positions with it (kv_pos gives absolute positions)
         if (!a.kv_pos) ps.g.pos_begin = static_cast<int32_t>(g.pos_begin - off);
-        ps.o_begin = made * a.num_q_rows + g.q_begin;
+        ps.o_begin = static_cast<int32_t>(made * P.part_rows + P.seg_row[i]);
         segs.push_back(ps);
       }
       P.seg_parts[i] = made;
@@ -273,15 +287,17 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
     }
     if (P.parts <= 1) {  // nothing long enough to split
       P.parts = 0;
+      P.part_rows = 0;
       P.seg_parts.clear();
+      P.seg_row.clear();
       segs.clear();
     }
   }
   if (P.parts > 0) {
     P.tile_rows = big;
     const size_t elt = a.o_dtype == CP_BF16 ? 2 : 4;
-    P.part_o_bytes = round256(static_cast<size_t>(P.parts) * a.num_q_rows * a.hq * a.dv * elt);
-    P.part_lse_bytes = round256(static_cast<size_t>(P.parts) * a.num_q_rows * a.hq * 4);
+    P.part_o_bytes = round256(static_cast<size_t>(P.parts) * P.part_rows * a.hq * a.dv * elt);
+    P.part_lse_bytes = round256(static_cast<size_t>(P.parts) * P.part_rows * a.hq * 4);
   } else {
     P.tile_rows = wgs_big < kSmallGridWorkgroups ? small : big;
     segs = plain_segs(a);
@@ -458,9 +474,9 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
   char *ws = static_cast<char *>(a->workspace);
   AttnParams q = p;
   const int o_bf16 = a->o_dtype == CP_BF16 ? 1 : 0;
-  const int64_t part_rows = static_cast<int64_t>(a->num_q_rows) * a->hq;  // (row, head) per part
+  const int64_t part_rows = P.part_rows * a->hq;  // (row, head) pairs per part
   if (P.parts > 0) {
-    // partial j of a segment's rows: rows j * num_q_rows + [q_begin, q_end)
+    // partial j of segment i's rows: compact rows j * part_rows + seg_row[i] + [0, q_len)
     q.o = ws + P.flag_bytes;
     q.o_rs = static_cast<int64_t>(a->hq) * a->dv;
     q.o_hs = a->dv;
@@ -478,13 +494,14 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
     const cp_segment &g = a->segs[i];
     const int32_t np = P.seg_parts[i];
     if (np == 0) continue;
-    const int64_t off = static_cast<int64_t>(g.q_begin) * a->hq;  // first (row, head) pair
+    const int64_t src = static_cast<int64_t>(P.seg_row[i]) * a->hq;  // first (row, head) pair
+    const int64_t dst = static_cast<int64_t>(g.q_begin) * a->hq;
     const size_t elt = o_bf16 ? 2 : 4;
     const hipError_t e = launch_lse_merge(
         np, static_cast<int64_t>(g.q_end - g.q_begin) * a->hq, a->dv,
-        static_cast<const char *>(q.o) + off * a->dv * elt, o_bf16, part_rows * a->dv,
-        q.lse + off, part_rows, static_cast<char *>(a->o) + off * a->dv * elt, o_bf16,
-        a->lse + off, s);
+        static_cast<const char *>(q.o) + src * a->dv * elt, o_bf16, part_rows * a->dv,
+        q.lse + src, part_rows, static_cast<char *>(a->o) + dst * a->dv * elt, o_bf16,
+        a->lse + dst, s);
     if (e != hipSuccess) return device_error(e);
   }
   return fill_empty_segments(a, s);

@@ -228,7 +228,10 @@ def test_split_workspace_size():
     kw = dict(num_q_rows=512, num_kv_rows=8192, hq=32, hkv=8, q_row_stride=32 * 128,
               k_row_stride=8 * 128, v_row_stride=8 * 128, o_row_stride=32 * 128,
               lse_row_stride=32, segs=segs, num_segs=1)
-    assert _ws(**kw) == (_lib.CP_OK, 2048 + 8 * 512 * 32 * 128 * 2 + 8 * 512 * 32 * 4)
+    split_bytes = 2048 + 8 * 512 * 32 * 128 * 2 + 8 * 512 * 32 * 4
+    assert _ws(**kw) == (_lib.CP_OK, split_bytes)
+    # partial rows cover only the segments' rows, not the whole output buffer
+    assert _ws(**dict(kw, num_q_rows=100000)) == (_lib.CP_OK, split_bytes)
     # non-dense output rows: no split, flags of the 4 x 32 128-row workgroups only
     assert _ws(**dict(kw, o_row_stride=32 * 128 + 8)) == (_lib.CP_OK, 512)
     # short keys: nothing to split

@@ -114,3 +114,27 @@ def test_split_repeatable_bitwise():
     o2, l2 = cp.attn_fwd(q, k, v, segs, 0.07)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_split_segments_at_offsets():
+    """Two requests' segments at rows [100, 400) and [500, 800) of a 900-row
+    output, each against its own keys (2400 and 3000, after cached
+    prefixes): the partials use compact rows, the merge writes the
+    segments' rows, and the gaps keep what they held."""
+    H, hkv, dqk, dv, n_q = 8, 2, 128, 128, 900
+    n_kv = 2400 + 3000
+    q, k, v = _tensors(n_q, n_kv, H, hkv, dqk, dv, seed=41)
+    segs = [cp.Segment(0, 100, 400, 2100, 1, 0, 2400),        # positions 2100..2399
+            cp.Segment(1, 500, 800, 2700, 1, 2400, 5400)]     # positions 2700..2999
+    o = torch.full((n_q, H, dv), -5.0, device=DEV, dtype=torch.float32)
+    lse = torch.full((n_q, H), 9.0, device=DEV, dtype=torch.float32)
+    assert _split_used(q, k, v, segs, o, lse)
+    say("split segments at row offsets")
+    cp.attn_fwd(q, k, v, segs, 0.09, o=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = ao.shard_attention(f64(q), f64(k), f64(v), [ix.Segment(*s.astuple()) for s in segs],
+                                H, hkv, 0.09)
+    rows = list(range(100, 400)) + list(range(500, 800))
+    compare(f64(o), f64(lse), ro, rl, rows, "bf16", "segments at offsets")
+    gap = torch.cat([torch.arange(0, 100), torch.arange(400, 500), torch.arange(800, 900)]).to(DEV)
+    assert torch.all(o[gap] == -5.0) and torch.all(lse[gap] == 9.0)
