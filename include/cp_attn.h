@@ -201,6 +201,10 @@ cp_status cp_ring_pad_len(int32_t cp_size, const int64_t *cached_per_rank, int64
  * kv_pos (if given) is indexed by logical row, per request:
  * kv_pos[req * block_table_stride * block_size + x].  Block ids outside the
  * pool are clamped into it (wrong values, never an out-of-bounds read).
+ * Requirements: block_size a multiple of 32, block_table_stride >= 1,
+ * num_kv_rows >= block_size (the pool holds num_kv_rows / block_size
+ * blocks), every segment with req >= 0, kv_begin a multiple of 32 and
+ * kv_end <= block_table_stride * block_size.
  * This is how a decode rank stores its shard when the cache is interleaved
  * over ranks in blocks ("What is Context Parallelism", section 2.2: token
  * blocks, not single tokens, on shard (i / block) mod W).
@@ -220,7 +224,7 @@ cp_status cp_ring_pad_len(int32_t cp_size, const int64_t *cached_per_rank, int64
  * segment; kv_pos is strictly increasing over every segment's kv range.
  *
  * segs is a HOST array (the planner's output); kv_pos is a DEVICE array
- * (int32, num_kv_rows entries) or NULL.  workspace is device memory of at
+ * (int32, num_kv_rows entries; paged KV: see above) or NULL.  workspace is device memory of at
  * least cp_attn_workspace_size bytes (NULL if that size is 0).
  *
  * Supported: dtype CP_BF16 with (dqk, dv) in {(64,64), (128,128), (192,128)}
@@ -276,10 +280,14 @@ cp_status cp_attn_workspace_size(const cp_attn_args *args, size_t *bytes);
 /*
  * cp_attn_fwd -- enqueue the attention described by `args` on `stream`.
  * Errors: CP_ERR_ARG (NULL pointers, hq % hkv != 0, a segment outside
- * [0, num_q_rows) or [0, num_kv_rows), negative sizes, pos_stride < 0,
- * misaligned pointers/strides), CP_ERR_UNSUPPORTED (dtype or head dims
- * without a kernel), CP_ERR_SMALL_BUFFER (workspace too small),
- * CP_ERR_DEVICE (launch failed).
+ * [0, num_q_rows) or [0, num_kv_rows) (paged KV: outside the request's
+ * logical rows), negative sizes, pos_stride < 0, positions outside
+ * [-2^29, 2^30), accumulate not 0 or 1, scale not positive and finite,
+ * misaligned pointers/strides, paged-KV requirements above not met),
+ * CP_ERR_UNSUPPORTED (dtype or head dims without a kernel, a block table
+ * with another shape than the MLA decode one, byte offsets of a tile or a
+ * decode segment beyond 32 bits), CP_ERR_SMALL_BUFFER (workspace too small
+ * or NULL when needed), CP_ERR_DEVICE (launch failed).
  */
 cp_status cp_attn_fwd(const cp_attn_args *args, void *stream);
 
@@ -298,7 +306,8 @@ cp_status cp_attn_fwd(const cp_attn_args *args, void *stream);
  * o_out: device [rows][heads][dv] of out_dtype; lse_out: device fp32
  *   [rows][heads] or NULL.  Outputs must not overlap the inputs.
  * Errors: CP_ERR_ARG (num_parts < 1, negative sizes, NULL pointers, strides
- *   smaller than a block, misaligned pointers or dv not a multiple of 8),
+ *   smaller than a block, misaligned pointers, dv not a multiple of 8 or
+ *   dv / 8 not a power of two up to 256),
  *   CP_ERR_UNSUPPORTED (a dtype other than CP_F32/CP_BF16), CP_ERR_DEVICE.
  */
 cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads,
