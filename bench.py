@@ -446,7 +446,7 @@ def _decode_paged(cp, w, bs):
     """Decode-CP rank 0 with the cache interleaved over the ranks in blocks
     of ``bs`` tokens (token i on rank (i // bs) mod W), its blocks scattered
     over a randomly allocated pool and read through a block table; the same
-    rows laid out contiguously are timed beside it."""
+    rows laid out contiguously are timed beside it, in alternating rounds."""
     import numpy as np
     import torch
     import workloads
@@ -476,11 +476,18 @@ def _decode_paged(cp, w, bs):
     a, keep = cp._lib.attn_args(q, pool, pool[:, :, :w.dv], segs_p, w.scale, o, lse, kv_pos=pos,
                                 block_table=bt, block_size=bs)
     ws = torch.empty(cp.attn_workspace_size(a), device="cuda", dtype=torch.uint8)
-    paged = _time_ms(lambda: cp.attn_fwd(q, pool, pool[:, :, :w.dv], segs_p, w.scale, kv_pos=pos,
-                                         o=o, lse=lse, workspace=ws, block_table=bt,
-                                         block_size=bs), reps=10)
-    cont = _time_ms(lambda: cp.attn_fwd(q, kc, kc[:, :, :w.dv], segs_c, w.scale, kv_pos=pos_c,
-                                        o=o, lse=lse, workspace=ws), reps=10)
+    fp = lambda: cp.attn_fwd(q, pool, pool[:, :, :w.dv], segs_p, w.scale, kv_pos=pos, o=o,
+                             lse=lse, workspace=ws, block_table=bt, block_size=bs)
+    fc = lambda: cp.attn_fwd(q, kc, kc[:, :, :w.dv], segs_c, w.scale, kv_pos=pos_c, o=o, lse=lse,
+                             workspace=ws)
+    # the two alternate in rounds (the GPU's clock drifts over a run, so two
+    # back-to-back blocks of calls would not compare like with like); the
+    # median round of each after two warm-up rounds
+    tp, tc = [], []
+    for r in range(7):
+        tp.append(_time_ms(fp, reps=4, warm=1 if r == 0 else 0))
+        tc.append(_time_ms(fc, reps=4, warm=1 if r == 0 else 0))
+    paged, cont = float(np.median(tp[2:])), float(np.median(tc[2:]))
     by = B * n * w.dqk * 2 + q.numel() * 2 + B * w.hq * (w.dv * 4 + 4)
     return {"block_size": bs, "rank_rows_per_request": n, "paged_ms": round(paged, 4),
             "contiguous_ms": round(cont, 4), "algorithmic_bytes": by,
