@@ -105,8 +105,10 @@ __device__ inline float sum_groups(float x) {
 // ds_read_b64_tr_b16 through inline asm.  The intrinsic makes the waitcnt pass
 // assume it may alias the LDS-DMA writes still in flight and drain them
 // (vmcnt(0)) before every use; the tile it reads was already completed by
-// an explicit vmcnt wait and a barrier.  Results are consumed only after
-// lds_wait(), which ties them to an lgkmcnt(0) by a data dependency.
+// an explicit vmcnt wait and a barrier.  The compiler does not count these
+// reads, so their results are consumed only after an explicit lgkmcnt wait
+// that takes the result registers as operands (the data dependency keeps
+// the consumers after it).
 __device__ inline u32x2 lds_read_tr16(const void *p) {
   u32x2 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1"
@@ -114,8 +116,15 @@ __device__ inline u32x2 lds_read_tr16(const void *p) {
                : "v"((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p));
   return r;
 }
-__device__ inline void lds_wait(u32x2 &a, u32x2 &b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+// The four reads in r are complete once at most 4 LDS operations issued
+// after them are pending: LDS operations complete in issue order, so while
+// one of r is pending all later ones are too.  (Operations the compiler adds
+// in between only make the wait stricter.)
+__device__ inline void lds_wait4_later(u32x2 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+}
+__device__ inline void lds_wait0(u32x2 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
 }
 
 // vmcnt wait with the other counters left alone (gfx9 encoding)
@@ -367,24 +376,35 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
     l_run += ls;
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
     // ---- O^T += V^T P^T : V^T from the same tile by transposing reads, in
-    // batches of 4 dv blocks
-    constexpr int PB = 4;
-#pragma unroll
-    for (int b0 = 0; b0 < OB; b0 += PB) {
-      u32x2 vl[PB], vh[PB];
+    // batches of 2 dv blocks, double-buffered: batch i + 1's reads are issued
+    // before the wait for batch i, so the reads of one batch run under the
+    // MFMAs of the previous one (4.7 % faster than batches of 4 with a full
+    // drain; deeper pipelines measured slower)
+    constexpr int PB = 2, NBT = OB / PB;
+    u32x2 vb[2][2 * PB];
+    auto pv_issue = [&](int bi, u32x2 (&r)[2 * PB]) {
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
-        const int b = b0 + j;
-        vl[j] = lds_read_tr16(tile + tr_base[b & 3] + 128 * (b >> 2));
-        vh[j] = lds_read_tr16(tile + tr_base[b & 3] + kRow16 + 128 * (b >> 2));
+        const int b = bi * PB + j;
+        r[2 * j] = lds_read_tr16(tile + tr_base[b & 3] + 128 * (b >> 2));
+        r[2 * j + 1] = lds_read_tr16(tile + tr_base[b & 3] + kRow16 + 128 * (b >> 2));
+      }
+    };
+    pv_issue(0, vb[0]);
+#pragma unroll
+    for (int bi = 0; bi < NBT; ++bi) {
+      u32x2 (&cur)[2 * PB] = vb[bi & 1];
+      if (bi + 1 < NBT) {
+        pv_issue(bi + 1, vb[(bi + 1) & 1]);
+        lds_wait4_later(cur);
+      } else {
+        lds_wait0(cur);
       }
 #pragma unroll
-      for (int j = 0; j < PB; ++j) lds_wait(vl[j], vh[j]);
-#pragma unroll
       for (int j = 0; j < PB; ++j) {
-        const u32x4 av = {vl[j][0], vl[j][1], vh[j][0], vh[j][1]};
+        const u32x4 av = {cur[2 * j][0], cur[2 * j][1], cur[2 * j + 1][0], cur[2 * j + 1][1]};
         const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-        oacc[b0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[b0 + j], 0, 0, 0);
+        oacc[bi * PB + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[bi * PB + j], 0, 0, 0);
       }
     }
   }
