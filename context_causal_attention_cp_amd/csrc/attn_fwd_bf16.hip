@@ -24,8 +24,9 @@
 //   * the loop is software-pipelined: the products of tile t + 1 run on the
 //     matrix cores while the exponentials of tile t run on the VALU;
 //   * exp2 with scale*log2(e) folded into one FMA; each row's reference max
-//     is fixed from its first tile (main pass), and a workgroup whose scores
-//     outgrow it by more than 2^64 is flagged and recomputed by an exact pass
+//     is fixed from its first tile (main pass), so later tiles take no row
+//     max at all; a workgroup where some row's sum of probabilities ends
+//     above 2^64 (or not finite) is flagged and recomputed by an exact pass
 //     that moves the reference (with an accumulator rescale) instead;
 //   * per wave, the number of visible tiles and of fully visible tiles is
 //     counted once up front from the tiles' first/last key positions (one
@@ -57,6 +58,7 @@ constexpr int NT = 64 * NW;    // threads
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescale = 8.0f;   // exact mode: log2 headroom before the reference moves
 constexpr float kGrowMax = 64.0f;  // main mode: log2 headroom before the workgroup is flagged
+constexpr float kMaxSum = 18446744073709551616.0f;  // 2^kGrowMax: largest accepted row sum
 constexpr int kNoPos = -(1 << 30);
 
 __device__ inline void map_work(int id, int num_tiles, int hq, int hkv, int &tile_order, int &h) {
@@ -204,10 +206,14 @@ struct Cfg {
 // (128-row workgroups, for launches too small to fill the chip otherwise).
 // EXACT = false: main pass; each row's softmax reference is the max of its
 //   first visible tile and never moves, so the accumulator is never rescaled
-//   (no VALU touches it inside the loop).  Probabilities stay finite and
-//   exact in relative terms while no score exceeds the reference by more than
-//   2^kGrowMax; a workgroup where one does writes a flag (p.ws, one int32 per
-//   workgroup of the launch).
+//   (no VALU touches it inside the loop) and later tiles need no row max.
+//   Probabilities stay finite and exact in relative terms while none exceeds
+//   2^kGrowMax.  Checked once at the end: every probability is at most its
+//   row's sum, so a workgroup where some row sum is above 2^kGrowMax (or not
+//   finite) writes a flag (p.ws, one int32 per workgroup of the launch).  A
+//   row of many moderately large probabilities can be flagged needlessly;
+//   the exact pass still gives the right result.  (Taking the row max of
+//   every tile instead cost 4 % of the kernel time.)
 // EXACT = true: recomputes only the flagged workgroups (the others return at
 //   once), moving the reference with an in-place rescale whenever a row
 //   outgrows it by more than 2^kRescale.
@@ -495,10 +501,10 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     pv(tc, 0, pf0);
     probs(cur, 1, pf1, ls);
     if (u >= n_full) mask(nxt, tn, u * BN);
-    rowmax(nxt, mx);
+    if (EXACT) rowmax(nxt, mx);
     pv(tc, 1, pf1);
     add_ls(ls);
-    return grows();
+    return EXACT ? grows() : false;
   };
   // move the reference max (rare): O and l of the rows scale by exp2(old - new)
   auto rescale = [&]() {
@@ -566,13 +572,18 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
 
   // ---- epilogue: normalise; O^T -> LDS -> whole output rows
   float inv[RB], lse[RB];
+  bool bad = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = sum_xor32(l_run[rb]);
     const bool any = l_tot > 0.f;
     inv[rb] = any ? 1.f / l_tot : 0.f;
     lse[rb] = any ? (m_ref[rb] + log2f(l_tot)) * kLn2 : -INFINITY;
+    // main pass: every probability is at most its row sum, so a sum above
+    // 2^kGrowMax (or not finite) means a score outgrew the reference
+    bad = bad || !(l_tot <= kMaxSum);
   }
+  if (!EXACT && __builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) s_flag = 1;
   __syncthreads();  // every wave is done with the tiles (and its flag is in)
   if (!EXACT) {
     const int flagged = s_flag;

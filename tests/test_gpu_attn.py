@@ -137,24 +137,28 @@ def test_repeatable_bitwise():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("rows,hq,val", [(300, 4, 0.1), (300, 4, 0.5), (4096, 128, 0.5)],
-                         ids=["small-2^27", "small-2^138", "large-2^138"])
-def test_reference_growth(rows, hq, val):
-    """A key, in a late tile, far above every score of the first tile: with
-    q = 1 and keys 0 except key 900 = val (192 dims, scale 1) the row max
-    grows by 192*val*log2(e) in log2 units -- 2^27 (kept by the main pass) or
-    2^138 (beyond fp32 exp range: the workgroup is flagged and recomputed).
-    128-row and 256-row workgroups; the plain definition decides."""
+@pytest.mark.parametrize("rows,hq,val,nbig", [(300, 4, 0.1, 1), (300, 4, 0.5, 1), (4096, 128, 0.5, 1),
+                                               (300, 4, 0.36, 1), (4096, 128, 0.23, 2)],
+                         ids=["small-2^27", "small-2^138", "large-2^138", "small-2^100",
+                              "large-2x2^63.6"])
+def test_reference_growth(rows, hq, val, nbig):
+    """Keys, in a late tile, far above every score of the first tile: with
+    q = 1 and keys 0 except keys 900.. = val (192 dims, scale 1) the row max
+    grows by 192*val*log2(e) in log2 units -- 2^27 (kept by the main pass),
+    2^100 or 2^138 (probabilities above 2^64, or beyond fp32 range: the
+    workgroup is flagged and recomputed), or twice 2^63.6 (no probability
+    above 2^64 but a row sum above it: flagged as well).  128-row and
+    256-row workgroups; the plain definition decides."""
     n_kv, dqk, dv = 1000, 192, 128
     g = torch.Generator(device=DEV)
     g.manual_seed(rows + hq)
     q = torch.ones((rows, hq, dqk), device=DEV, dtype=torch.bfloat16)
     k = torch.zeros((n_kv, hq, dqk), device=DEV, dtype=torch.bfloat16)
-    k[900] = val
+    k[900:900 + nbig] = val
     v = torch.randn((n_kv, hq, dv), generator=g, device=DEV).to(torch.bfloat16)
     # every row sees all keys (positions n_kv .. n_kv + rows - 1)
     segs = [cp.Segment(0, 0, rows, n_kv, 1, 0, n_kv)]
-    say(f"reference growth rows={rows} hq={hq} val={val}")
+    say(f"reference growth rows={rows} hq={hq} val={val} keys={nbig}")
     o, lse = cp.attn_fwd(q, k, v, segs, 1.0)
     torch.cuda.synchronize()
     sample = sorted(set([0, 1, rows // 2, rows - 1]))
