@@ -101,8 +101,9 @@ __device__ inline float sum_xor32(float x) {
 // ds_read_b64_tr_b16 through inline asm.  The intrinsic makes the waitcnt pass
 // assume it may alias the LDS-DMA writes still in flight and drain them
 // (vmcnt(0)) before every use; the tile it reads was already completed by
-// an explicit vmcnt wait and a barrier.  Results are consumed only after
-// lds_wait(), which ties them to an lgkmcnt(0) by a data dependency.
+// an explicit vmcnt wait and a barrier.  The compiler does not count these
+// reads: their results are consumed only after an explicit lgkmcnt wait
+// that takes the result registers as operands.
 __device__ inline u32x2 lds_read_tr16(const void *p) {
   u32x2 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1"
@@ -110,8 +111,27 @@ __device__ inline u32x2 lds_read_tr16(const void *p) {
                : "v"((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p));
   return r;
 }
-__device__ inline void lds_wait(u32x2 &a, u32x2 &b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+// The reads in vl/vh are complete once at most LATER LDS operations issued
+// after them are pending: LDS operations complete in issue order, so while
+// one of them is pending all later ones are too.  (Reads the compiler issues
+// in between only make the wait stricter.)
+template <int LATER>
+__device__ inline void lds_wait_later(u32x2 (&vl)[4], u32x2 (&vh)[4]) {
+  static_assert(LATER == 0 || LATER == 8, "count");
+  if constexpr (LATER == 8)
+    asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(vl[0]), "+v"(vl[1]), "+v"(vl[2]), "+v"(vl[3]),
+                 "+v"(vh[0]), "+v"(vh[1]), "+v"(vh[2]), "+v"(vh[3]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vl[0]), "+v"(vl[1]), "+v"(vl[2]), "+v"(vl[3]),
+                 "+v"(vh[0]), "+v"(vh[1]), "+v"(vh[2]), "+v"(vh[3]));
+}
+template <int LATER>
+__device__ inline void lds_wait_later(u32x2 (&vl)[2], u32x2 (&vh)[2]) {
+  static_assert(LATER == 0 || LATER == 4, "count");
+  if constexpr (LATER == 4)
+    asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(vl[0]), "+v"(vl[1]), "+v"(vh[0]), "+v"(vh[1]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vl[0]), "+v"(vl[1]), "+v"(vh[0]), "+v"(vh[1]));
 }
 
 template <int N>
@@ -451,17 +471,16 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
       pf[rb] = __builtin_bit_cast(bf16x8, pk);
     }
   };
-  // O^T += V^T P^T for 16-key step c of the tile at tl
-  auto pv = [&](const char *tl, int c, const bf16x8 (&pf)[RB]) {
-    u32x2 vl[OB], vh[OB];
+  // V^T fragments of 16-key step c of the tile at tl (issued; consumed by pv_mma)
+  auto pv_read = [&](const char *tl, int c, u32x2 (&vl)[OB], u32x2 (&vh)[OB]) {
 #pragma unroll
     for (int b = 0; b < OB; ++b) {
       const char *vp = tl + vt + 64 * (4 * VCH * c + 4 * b);
       vl[b] = lds_read_tr16(vp);
       vh[b] = lds_read_tr16(vp + 64 * 2 * VCH);
     }
-#pragma unroll
-    for (int b = 0; b < OB; ++b) lds_wait(vl[b], vh[b]);
+  };
+  auto pv_mma = [&](u32x2 (&vl)[OB], u32x2 (&vh)[OB], const bf16x8 (&pf)[RB]) {
 #pragma unroll
     for (int b = 0; b < OB; ++b) {
       const u32x4 av = {vl[b][0], vl[b][1], vh[b][0], vh[b][1]};
@@ -470,6 +489,13 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
       for (int rb = 0; rb < RB; ++rb)
         oacc[b][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb], oacc[b][rb], 0, 0, 0);
     }
+  };
+  // O^T += V^T P^T for 16-key step c of the tile at tl, reads and products
+  auto pv = [&](const char *tl, int c, const bf16x8 (&pf)[RB]) {
+    u32x2 vl[OB], vh[OB];
+    pv_read(tl, c, vl, vh);
+    lds_wait_later<0>(vl, vh);
+    pv_mma(vl, vh, pf);
   };
   auto stage = [&](int t) { return (const char *)sm[t % NBUF]; };
   float mx[RB];
@@ -496,13 +522,20 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     // scheduling hint: interleave the products with the LDS reads and the
     // exponentials of this block (measured: +2-3 % over the default order)
     __builtin_amdgcn_iglp_opt(0);
+    // the V^T reads of the second key step go out before the wait for the
+    // first one's (1.5 % faster than draining after each step's reads)
+    u32x2 vl0[OB], vh0[OB], vl1[OB], vh1[OB];
     qk(nxt, tn);
+    pv_read(tc, 0, vl0, vh0);
     probs(cur, 0, pf0, ls);
-    pv(tc, 0, pf0);
+    pv_read(tc, 1, vl1, vh1);
+    lds_wait_later<2 * OB>(vl0, vh0);  // the second step's reads may be pending
+    pv_mma(vl0, vh0, pf0);
     probs(cur, 1, pf1, ls);
     if (u >= n_full) mask(nxt, tn, u * BN);
     if (EXACT) rowmax(nxt, mx);
-    pv(tc, 1, pf1);
+    lds_wait_later<0>(vl1, vh1);
+    pv_mma(vl1, vh1, pf1);
     add_ls(ls);
     return EXACT ? grows() : false;
   };
