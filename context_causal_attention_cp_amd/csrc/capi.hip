@@ -161,13 +161,26 @@ std::vector<PlanSeg> plain_segs(const cp_attn_args &a) {
 
 // Splits the non-empty segments into launches of at most kMaxLaunchSegs,
 // heaviest first (largest visible KV extent), numbering their tiles.
-std::vector<LaunchSegs> plan_launches(const std::vector<PlanSeg> &segs, int tile_rows) {
+std::vector<LaunchSegs> plan_launches(const std::vector<PlanSeg> &segs, int tile_rows,
+                                      bool causal) {
   std::vector<int32_t> order;
   for (size_t i = 0; i < segs.size(); ++i)
     if (segs[i].g.q_end > segs[i].g.q_begin && segs[i].g.kv_end > segs[i].g.kv_begin)
       order.push_back(static_cast<int32_t>(i));
+  // segments with the most work first (the kernel starts the heaviest query
+  // tiles of a segment first; across segments this order decides): more keys
+  // first, and among equal key ranges of a causal call the later positions
+  // (key positions increase, so a later row sees at least as many keys)
+  auto last_pos = [&](int32_t x) {
+    const cp_segment &g = segs[x].g;
+    return static_cast<int64_t>(g.pos_begin) +
+           static_cast<int64_t>(g.q_end - g.q_begin - 1) * g.pos_stride;
+  };
   std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-    return segs[x].g.kv_end - segs[x].g.kv_begin > segs[y].g.kv_end - segs[y].g.kv_begin;
+    const int32_t kx = segs[x].g.kv_end - segs[x].g.kv_begin;
+    const int32_t ky = segs[y].g.kv_end - segs[y].g.kv_begin;
+    if (kx != ky) return kx > ky;
+    return causal && last_pos(x) > last_pos(y);
   });
   std::vector<LaunchSegs> out;
   for (size_t i = 0; i < order.size(); i += kMaxLaunchSegs) {
@@ -302,7 +315,7 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
     P.tile_rows = wgs_big < kSmallGridWorkgroups ? small : big;
     segs = plain_segs(a);
   }
-  P.launches = plan_launches(segs, P.tile_rows);
+  P.launches = plan_launches(segs, P.tile_rows, a.causal != 0);
   int64_t wgs = 0;
   for (const LaunchSegs &L : P.launches) wgs += static_cast<int64_t>(L.num_tiles) * a.hq;
   // one int32 flag per workgroup of every launch (16-byte rounded; the
@@ -460,7 +473,7 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
     return fill_empty_segments(a, s);
   }
   if (path == Path::F32) {
-    for (const LaunchSegs &L : plan_launches(plain_segs(*a), attn_f32_tile_rows(a->dqk))) {
+    for (const LaunchSegs &L : plan_launches(plain_segs(*a), attn_f32_tile_rows(a->dqk), a->causal != 0)) {
       const hipError_t e = launch_attn_f32(p, L, a->dqk, s);
       if (e != hipSuccess) return device_error(e);
     }
