@@ -325,7 +325,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (valid[rb]) x = *(const u32x4 *)(qp + 16 * s);
+      if (valid[rb] && n_vis > 0) x = *(const u32x4 *)(qp + 16 * s);  // no key: Q unused
       qf[rb][s] = __builtin_bit_cast(bf16x8, x);
     }
   }
