@@ -90,7 +90,7 @@ def main():
     a = _args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: every CP rank's share is a separate launch on "
-              f"that GPU, so --gpus {a.gpus} is not a configuration this build measures.",
+              f"that GPU, so --gpus {a.gpus} is not a configuration it measures.",
               file=sys.stderr)
         sys.exit(2)
     if a.copy_calibration:
