@@ -95,6 +95,43 @@ def test_ring_partials_with_key_positions(dqk, dv):
         compare(f64(mo), f64(ml), dense_o, dense_l, range(len(mine)), "bf16", "merged")
 
 
+@pytest.mark.parametrize("case", ["ring-diagonal", "zigzag-prefix", "interleave-varlen", "split"])
+def test_segment_order_invariant(case):
+    """The planner reorders a launch's segments (most keys first; among
+    equal key ranges of a causal call, later positions first).  Passing the
+    segments in the opposite order must give bit-identical O and LSE: every
+    row is computed by one workgroup over the same tiles whatever the order."""
+    H, dqk, dv = 4, 192, 128
+    scale = 1.0 / np.sqrt(dqk)
+    kv_pos = None
+    if case == "ring-diagonal":      # rank 0's own zigzag pair: equal key ranges
+        C, T = 4, 2048
+        q, k, v = _tensors(T, T, H, H, dqk, dv, "bf16", seed=61)
+        plan = cp.shard_plan("zigzag", C, 0, [T], [0])
+        idx = torch.from_numpy(plan.global_idx.astype(np.int64)).to(DEV)
+        q, k, v, kv_pos = q.index_select(0, idx), k.index_select(0, idx), v.index_select(0, idx), \
+            idx.to(torch.int32)
+        segs = [cp.Segment(s.req, s.q_begin, s.q_end, s.pos_begin, s.pos_stride, 0, plan.num_local)
+                for s in plan.segments]
+    elif case == "split":            # small call: keys split into chunks
+        q, k, v = _tensors(600, 5000, H, H, dqk, dv, "bf16", seed=62)
+        segs = [cp.Segment(0, 0, 300, 2200, 1, 0, 2500), cp.Segment(1, 300, 600, 2200, 1, 2500, 5000)]
+    else:
+        strategy = "zigzag" if case == "zigzag-prefix" else "interleave"
+        lens, pre = ([3000], [500]) if strategy == "zigzag" else ([700, 5, 1300, 2000], [100, 0, 900, 0])
+        C = 2 if strategy == "zigzag" else 3
+        n_kv = sum(lens) + sum(pre)
+        q, k, v = _tensors(sum(lens), n_kv, H, 2, dqk, dv, "bf16", seed=63)
+        plan = cp.shard_plan(strategy, C, 1, lens, pre)
+        q = q.index_select(0, torch.from_numpy(plan.global_idx.astype(np.int64)).to(DEV))
+        segs = plan.segments
+    say(f"segment order {case}: {len(segs)} segments")
+    o1, l1 = cp.attn_fwd(q, k, v, list(segs), scale, kv_pos=kv_pos)
+    o2, l2 = cp.attn_fwd(q, k, v, list(segs)[::-1], scale, kv_pos=kv_pos)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_empty_kv_segment_and_noncausal_and_f32_out():
     hq = hkv = 2
     q, k, v = _tensors(40, 64, hq, hkv, 128, 128, "bf16", seed=5)
