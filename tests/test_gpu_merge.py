@@ -74,3 +74,30 @@ def test_merge_repeatable():
     b = cp.lse_merge(o, lse)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_merge_random_config(seed):
+    """Seeded random shapes: 1..16 partials, ragged rows and heads, every
+    allowed dv (8 x a power of two up to 2048), mixed part / output dtypes,
+    0..60 % empty partials."""
+    rng = np.random.default_rng(3000 + seed)
+    P = int(rng.integers(1, 17))
+    rows, heads = int(rng.integers(1, 300)), int(rng.integers(1, 24))
+    dv = int(8 * 2 ** rng.integers(0, 9))
+    pdt = (torch.bfloat16, torch.float32)[int(rng.integers(0, 2))]
+    odt = (torch.bfloat16, torch.float32)[int(rng.integers(0, 2))]
+    empty = float(rng.uniform(0.0, 0.6))
+    say(f"merge random {seed}: P={P} rows={rows} heads={heads} dv={dv} {pdt}->{odt} empty={empty:.2f}")
+    o, lse = _parts(P, rows, heads, dv, pdt, seed=4000 + seed, empty_frac=empty)
+    mo, ml = cp.lse_merge(o, lse, out_dtype=odt)
+    torch.cuda.synchronize()
+    ro, rl = ao.lse_merge(f64(o), f64(lse))
+    tol = 2e-2 if odt == torch.bfloat16 else 1e-5
+    fin = np.isfinite(rl)
+    got = f64(ml)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.max(np.abs(f64(mo) - ro)) <= tol
+    if fin.any():
+        assert float(np.max(np.abs(got[fin] - rl[fin]))) <= 1e-5
+    assert np.all(f64(mo)[~fin] == 0)
