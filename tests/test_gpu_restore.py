@@ -61,3 +61,26 @@ def test_restore_apply_empty():
     src = torch.zeros((4, 8), device=DEV)
     out = cp.restore_apply(torch.zeros((0,), device=DEV, dtype=torch.int32), src)
     assert out.shape == (0, 8)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_restore_apply_random_plan(seed):
+    """Seeded random plans: strategy, CP size, 1..6 requests of 1..3000
+    tokens; the rank-major gathered rows (int32 rows of 16 B .. 12 KiB whose
+    first element is the token's global index) restored to causal order."""
+    rng = np.random.default_rng(5000 + seed)
+    strategy = ("zigzag", "interleave")[int(rng.integers(0, 2))]
+    C = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    lens = [int(x) for x in rng.integers(1, 3001, size=int(rng.integers(1, 7)))]
+    row_elems = 4 * int(rng.integers(1, 769))
+    say(f"restore random {seed}: {strategy} C={C} lens={lens} row_bytes={4 * row_elems}")
+    restore, pad = cp.restore_index(strategy, C, lens)
+    gathered = np.array(ix.gathered_global_idx(strategy, C, lens), dtype=np.int64)
+    assert np.array_equal(restore, np.array(ix.restore_index(strategy, C, lens)[0], dtype=np.int32))
+    src = torch.from_numpy(gathered.astype(np.int32)).to(DEV).view(-1, 1).repeat(1, row_elems)
+    src[:, 1:] += torch.arange(1, row_elems, device=DEV, dtype=torch.int32)
+    out = cp.restore_apply(torch.from_numpy(restore.astype(np.int32)).to(DEV), src)
+    torch.cuda.synchronize()
+    want = so.restore_apply(restore, src.cpu().numpy())
+    assert np.array_equal(out.cpu().numpy(), want)
+    assert np.array_equal(out[:, 0].cpu().numpy(), np.arange(sum(lens), dtype=np.int32))
