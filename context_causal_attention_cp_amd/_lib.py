@@ -215,11 +215,12 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _stream(stream):
+    return _torch().cuda.current_stream() if stream is None else stream
+
+
 def _stream_handle(stream) -> int:
-    torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return int(stream.cuda_stream)
+    return int(_stream(stream).cuda_stream)
 
 
 def _segments_arg(segs):
@@ -312,17 +313,22 @@ def attn_fwd(q, k, v, segs, scale: float, causal: bool = True, kv_pos=None, o=No
     if accumulate and (o is None or lse is None):
         raise ValueError("accumulate needs the running o and lse")
     torch = _torch()
-    if o is None:
-        o = torch.empty((q.shape[0], q.shape[1], v.shape[2]), device=q.device,
-                        dtype=o_dtype if o_dtype is not None else q.dtype)
-    if lse is None:
-        lse = torch.empty((q.shape[0], q.shape[1]), device=q.device, dtype=torch.float32)
-    a, keep = attn_args(q, k, v, segs, scale, o, lse, causal, kv_pos, workspace, accumulate,
-                        block_table, block_size)
-    need = attn_workspace_size(a)
-    if need and (workspace is None or a.workspace_bytes < need):
-        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    stream = _stream(stream)
+    # buffers allocated here belong to the stream the kernels run on: the
+    # caching allocator then hands a freed block to other work only in that
+    # stream's order, never while these kernels may still use it
+    with torch.cuda.stream(stream):
+        if o is None:
+            o = torch.empty((q.shape[0], q.shape[1], v.shape[2]), device=q.device,
+                            dtype=o_dtype if o_dtype is not None else q.dtype)
+        if lse is None:
+            lse = torch.empty((q.shape[0], q.shape[1]), device=q.device, dtype=torch.float32)
+        a, keep = attn_args(q, k, v, segs, scale, o, lse, causal, kv_pos, workspace, accumulate,
+                            block_table, block_size)
+        need = attn_workspace_size(a)
+        if need and (workspace is None or a.workspace_bytes < need):
+            workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+            a.workspace, a.workspace_bytes = workspace.data_ptr(), need
     s = _lib.cp_attn_fwd(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream)))
     del keep
     if s != CP_OK:
@@ -341,11 +347,13 @@ def lse_merge(o_parts, lse_parts, out_dtype=None, o_out=None, lse_out=None, stre
         raise ValueError("lse_parts must be fp32 [P, rows, heads]")
     if not (o_parts[0].is_contiguous() and lse_parts[0].is_contiguous()):
         raise ValueError("each partial must be contiguous")
-    if o_out is None:
-        o_out = torch.empty((rows, heads, dv), device=o_parts.device,
-                            dtype=out_dtype if out_dtype is not None else o_parts.dtype)
-    if lse_out is None:
-        lse_out = torch.empty((rows, heads), device=o_parts.device, dtype=torch.float32)
+    stream = _stream(stream)
+    with torch.cuda.stream(stream):   # outputs made here belong to the kernel's stream
+        if o_out is None:
+            o_out = torch.empty((rows, heads, dv), device=o_parts.device,
+                                dtype=out_dtype if out_dtype is not None else o_parts.dtype)
+        if lse_out is None:
+            lse_out = torch.empty((rows, heads), device=o_parts.device, dtype=torch.float32)
     if not o_out.is_contiguous() or not lse_out.is_contiguous():
         raise ValueError("outputs must be contiguous")
     s = _lib.cp_lse_merge(P, rows, heads, dv, o_parts.data_ptr(), _dtype_code(o_parts),
@@ -365,8 +373,10 @@ def restore_apply(index, src, out=None, stream=None):
     if src.dim() < 1 or not src[0:1].is_contiguous():
         raise ValueError("src rows must be contiguous")
     n = index.shape[0]
+    stream = _stream(stream)
     if out is None:
-        out = torch.empty((n,) + tuple(src.shape[1:]), device=src.device, dtype=src.dtype)
+        with torch.cuda.stream(stream):   # belongs to the kernel's stream
+            out = torch.empty((n,) + tuple(src.shape[1:]), device=src.device, dtype=src.dtype)
     row_bytes = src[0:1].numel() * src.element_size() if src.shape[0] else 0
     s = _lib.cp_restore_apply(index.data_ptr(), n, src.data_ptr(), src.shape[0],
                               src.stride(0) * src.element_size(), out.data_ptr(),

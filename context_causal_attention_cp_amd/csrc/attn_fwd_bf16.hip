@@ -616,6 +616,20 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
     // 2^kGrowMax (or not finite) means a score outgrew the reference
     bad = bad || !(l_tot <= kMaxSum);
   }
+  if (!EXACT) {
+    // probabilities within range can still carry huge values of V past the
+    // fp32 range (|v| > 2^128 / row sum): such an accumulator is flagged too,
+    // and the exact pass, whose probabilities stay below 2^kRescale,
+    // recomputes it (the exact output is a convex combination of V rows)
+    bool fin = true;
+#pragma unroll
+    for (int b = 0; b < OB; ++b)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) fin = fin && __builtin_isfinite(oacc[b][rb][i]);
+    bad = bad || !fin;
+  }
   if (!EXACT && __builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) s_flag = 1;
   __syncthreads();  // every wave is done with the tiles (and its flag is in)
   if (!EXACT) {

@@ -2,8 +2,8 @@
 //
 // "What is Context Parallelism" (blog), section 3.6: the ring rounds (pass-KV)
 // and the KV shards (pass-Q, decode CP) each give a normalised partial O_j
-// with its log-sum L_j, and the exact result is their merge, the
-// generalisation of the online softmax.  Per (row, head):
+// with its log-sum L_j, and the exact result is their merge: the online
+// softmax's rescaling applied to whole partial results.  Per (row, head):
 //   m = max_j L_j,  w_j = exp(L_j - m),  O = sum_j w_j O_j / sum_j w_j,
 //   L = m + ln sum_j w_j.
 // A partial with L_j = -inf has w_j = 0 and its O_j is never read.

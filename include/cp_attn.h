@@ -24,9 +24,11 @@
  *
  * Conventions shared by every call:
  *   - Ownership: the caller owns every buffer (host and device) and the
- *     stream.  The library keeps no state between calls and allocates no
- *     device memory; scratch comes from a caller workspace whose size
- *     cp_attn_workspace_size reports.
+ *     stream.  The library allocates no device memory; scratch comes from a
+ *     caller workspace whose size cp_attn_workspace_size reports.  What it
+ *     keeps between calls is only the text of the calling thread's last
+ *     device error (thread-local, read by cp_last_error); no result of a
+ *     call depends on an earlier call.
  *   - Errors: every call returns a cp_status and never throws.  Arguments
  *     are checked on the host before anything is enqueued; on an error
  *     nothing is enqueued.  CP_ERR_SMALL_BUFFER still writes the required

@@ -21,7 +21,8 @@ What is computed, written out from its definition:
   its log-sum L_j): the formula above with V(i) restricted to the subset.
 * The log-sum-exp merge (same blog, section 3.6; the page lost the display
   formula in extraction, so this is the reading from the surrounding text,
-  "the generalisation of FlashAttention's online softmax"):
+  which presents the merge as FlashAttention's online-softmax rescaling
+  applied to whole partial results):
       L = ln sum_j exp(L_j),   O = sum_j exp(L_j - L) * O_j
   computed with m = max_j L_j; partials with L_j = -inf contribute nothing;
   all partials empty gives O = 0, L = -inf.

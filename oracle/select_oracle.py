@@ -8,10 +8,13 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 * passing Q gives the smaller message iff T / (T + P) <= 2 * N_kv / N_h
   (the section's threshold is 12.5 % for N_h = 128, N_kv = 8);
 * the empirical fit h(T, P) = -1.059 log T + 1.145 log(T / (T + P)) + 12.112,
-  h > 0 choosing pass-KV.  Parity unpinned: the pages fix no value of h, and
-  the switch point they quote (about 5 % miss rate at 128K tokens, CP 4) is
+  h > 0 choosing pass-KV.  The pages print the coefficients and the constant
+  but no value of h and no log base; what they fix holds under any base and
+  is pinned (constant, ratio of the coefficients, signs, logarithmic form).
+  The base is a reading: natural logarithm, parity unpinned (the switch
+  point quoted beside the fit, about 5 % miss rate at 128K tokens, CP 4, is
   not reproduced by the printed fit under a natural, base-2 or base-10
-  logarithm; this oracle reads log as the natural logarithm;
+  logarithm);
 * ring messages are padded to max_i P_i + ceil(T / N).
 
 Section 2.1 (engineering notes) / 5.1: the rank-major all-gathered rows,

@@ -1,7 +1,9 @@
 """Helpers shared by the GPU parity tests (not collected: no test_ prefix)."""
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -71,3 +73,34 @@ def oracle_attention(q_loc64, k64, v64, segs, hq, hkv, scale, rows=None, kv_pos=
                      causal=True):
     return ao.shard_attention(q_loc64, k64, v64, segs, hq, hkv, scale, kv_pos=kv_pos,
                               rows=rows, causal=causal)
+
+
+def par_map(fn, items, workers=None):
+    """fn over items in a thread pool (NumPy's kernels release the GIL), with
+    one BLAS thread per worker; results in the order of items.  The oracle's
+    arithmetic is unchanged: the work items are independent heads or row
+    blocks of the same definition."""
+    from threadpoolctl import threadpool_limits
+    items = list(items)
+    if workers is None:
+        workers = int(os.environ.get("CPATTN_ORACLE_THREADS", "0")) or \
+            min(16, len(os.sched_getaffinity(0)))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max(1, workers)) as ex:
+        return list(ex.map(fn, items))
+
+
+def chunks(xs, n):
+    xs = list(xs)
+    return [xs[i:i + n] for i in range(0, len(xs), n)]
+
+
+def bf16_host(t) -> np.ndarray:
+    """A bf16 tensor's bit patterns on the host (uint16 array, same shape)."""
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 values of bf16 bit patterns (a bf16 is the upper half
+    of the fp32 with the same bits)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -174,18 +174,25 @@ def test_repeatable_bitwise():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("rows,hq,val,nbig", [(300, 4, 0.1, 1), (300, 4, 0.5, 1), (4096, 128, 0.5, 1),
-                                               (300, 4, 0.36, 1), (4096, 128, 0.23, 2)],
-                         ids=["small-2^27", "small-2^138", "large-2^138", "small-2^100",
-                              "large-2x2^63.6"])
-def test_reference_growth(rows, hq, val, nbig):
+GROWTH = [(300, 4, 0.1, 1), (300, 4, 0.5, 1), (4096, 128, 0.5, 1), (300, 4, 0.36, 1),
+          (4096, 128, 0.23, 2)]
+GROWTH_IDS = ["small-2^27", "small-2^138", "large-2^138", "small-2^100", "large-2x2^63.6"]
+
+
+@pytest.mark.parametrize("accumulate", [False, True], ids=["write", "accumulate"])
+@pytest.mark.parametrize("rows,hq,val,nbig", GROWTH, ids=GROWTH_IDS)
+def test_reference_growth(rows, hq, val, nbig, accumulate):
     """Keys, in a late tile, far above every score of the first tile: with
     q = 1 and keys 0 except keys 900.. = val (192 dims, scale 1) the row max
     grows by 192*val*log2(e) in log2 units -- 2^27 (kept by the main pass),
     2^100 or 2^138 (probabilities above 2^64, or beyond fp32 range: the
     workgroup is flagged and recomputed), or twice 2^63.6 (no probability
     above 2^64 but a row sum above it: flagged as well).  128-row and
-    256-row workgroups; the plain definition decides."""
+    256-row workgroups; the plain definition decides.
+    accumulate: keys 0..449 are first written by a plain call, then keys
+    450..999 (with the large ones) are merged into that running (O, LSE) by
+    an accumulating call; a flagged workgroup must merge exactly once (in
+    the exact pass), which the dense result over all keys checks."""
     n_kv, dqk, dv = 1000, 192, 128
     g = torch.Generator(device=DEV)
     g.manual_seed(rows + hq)
@@ -193,10 +200,18 @@ def test_reference_growth(rows, hq, val, nbig):
     k = torch.zeros((n_kv, hq, dqk), device=DEV, dtype=torch.bfloat16)
     k[900:900 + nbig] = val
     v = torch.randn((n_kv, hq, dv), generator=g, device=DEV).to(torch.bfloat16)
-    # every row sees all keys (positions n_kv .. n_kv + rows - 1)
-    segs = [cp.Segment(0, 0, rows, n_kv, 1, 0, n_kv)]
-    say(f"reference growth rows={rows} hq={hq} val={val} keys={nbig}")
-    o, lse = cp.attn_fwd(q, k, v, segs, 1.0)
+    say(f"reference growth rows={rows} hq={hq} val={val} keys={nbig} accumulate={accumulate}")
+    if not accumulate:
+        # every row sees all keys (positions n_kv .. n_kv + rows - 1)
+        segs = [cp.Segment(0, 0, rows, n_kv, 1, 0, n_kv)]
+        o, lse = cp.attn_fwd(q, k, v, segs, 1.0)
+    else:
+        cut = 450
+        pos = torch.arange(n_kv, device=DEV, dtype=torch.int32)
+        o, lse = cp.attn_fwd(q, k[:cut], v[:cut], [cp.Segment(0, 0, rows, n_kv, 1, 0, cut)], 1.0,
+                             kv_pos=pos[:cut].contiguous())
+        cp.attn_fwd(q, k[cut:], v[cut:], [cp.Segment(0, 0, rows, n_kv, 1, 0, n_kv - cut)], 1.0,
+                    kv_pos=pos[cut:].contiguous(), o=o, lse=lse, accumulate=True)
     torch.cuda.synchronize()
     sample = sorted(set([0, 1, rows // 2, rows - 1]))
     q64, k64, v64 = f64(q), f64(k), f64(v)
@@ -205,6 +220,37 @@ def test_reference_growth(rows, hq, val, nbig):
                            np.arange(n_kv), 1.0)
         compare(f64(o[sample, h]), f64(lse[sample, h]), ro, rl, range(len(sample)), "bf16",
                 f"head {h}")
+
+
+@pytest.mark.parametrize("rows,hq", [(300, 4), (4096, 128)], ids=["128-row", "256-row"])
+def test_huge_values_overflow_guard(rows, hq):
+    """Probabilities within the main pass's range (a key 2^60 above the
+    first tile's scores) times value rows near 2^70 overflow an fp32
+    accumulator (2^130) although the exact output, a convex combination of
+    V rows, is finite: the workgroup must be flagged and recomputed.  Values
+    are O(2^70), so O is compared after scaling by 2^-70 (the output is
+    linear in V), with the bf16 tolerance."""
+    n_kv, dqk, dv, big = 1000, 192, 128, 2.0 ** 70
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7 + rows)
+    q = torch.ones((rows, hq, dqk), device=DEV, dtype=torch.bfloat16)
+    k = torch.zeros((n_kv, hq, dqk), device=DEV, dtype=torch.bfloat16)
+    k[900] = 0.2166          # bf16 0.216797: growth 192 * 0.216797 * log2(e) = 2^60.05
+    v = torch.randn((n_kv, hq, dv), generator=g, device=DEV)
+    v[880:920] *= big        # the large key's row and its neighbours
+    v = v.to(torch.bfloat16)
+    segs = [cp.Segment(0, 0, rows, n_kv, 1, 0, n_kv)]
+    say(f"huge values rows={rows} hq={hq}")
+    o, lse = cp.attn_fwd(q, k, v, segs, 1.0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all()), "non-finite O"
+    sample = sorted(set([0, 1, rows // 2, rows - 1]))
+    q64, k64, v64 = f64(q), f64(k), f64(v)
+    for h in sorted(set([0, hq - 1])):
+        ro, rl = ao.attend(q64[sample, h], k64[:, h], v64[:, h], [n_kv + i for i in sample],
+                           np.arange(n_kv), 1.0)
+        compare(f64(o[sample, h]) / big, f64(lse[sample, h]), ro / big, rl, range(len(sample)),
+                "bf16", f"head {h} (O / 2^70)")
 
 
 @pytest.mark.parametrize("dqk,dv,dtype,odt,C,T,H", [

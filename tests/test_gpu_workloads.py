@@ -1,8 +1,19 @@
 """GPU parity on the full-size workloads, through the C ABI, in the launch
-configuration the bench times.  Rows the oracle can afford are compared
-element by element (all rows for the small workloads, seeded samples plus
-every segment's first and last row for the large ones); the closed form
-LSE = ln(#visible keys) for q = 0 checks the mask on every row."""
+configuration the bench times.  Rows are compared element by element with
+the fp64 oracle, all heads:
+
+* 256 tokens (fp32) and 8192 tokens after a 1024-token prefix: every row of
+  every rank;
+* the 12-request interleave batch: every row of requests 0 and 1 and of the
+  two longest requests, 256 seeded rows of each other segment plus its
+  first and last row, every rank;
+* 131072 tokens (MLA prefill), ranks 0, 3 and 7: 256 seeded rows per zigzag
+  block plus its first and last row, for each of the 8 ring partials, their
+  LSE merge, the direct call over the full KV and (rank 0) the 8 partials
+  accumulated in place.
+
+The closed form LSE = ln(#visible keys) for q = 0 checks the mask on every
+row.  The oracle runs heads (and row blocks) in a thread pool."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +22,8 @@ import context_causal_attention_cp_amd as cp
 import workloads
 from oracle import attn_oracle as ao
 from oracle import index_oracle as ix
-from gpu_helpers import compare, f64, oracle_segments, sample_rows, say
+from gpu_helpers import (bf16_bits_f64, bf16_host, chunks, compare, f64, oracle_segments, par_map,
+                         sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -60,124 +72,165 @@ def test_zigzag_t256_all_ranks_restore_vs_dense():
             dense_o, dense_l, range(w.total_new), "f32", "restored vs dense")
 
 
-def test_zigzag_t8192_p1024():
-    w = workloads.get("zigzag_t8192_p1024")
-    say(f"workload {w.name}")
+def _oracle_rows(q_loc64_h, k_h, v_h, segs, scale, rows, kv_pos=None, block=1024):
+    """Oracle (O, LSE) of one head for the local rows ``rows`` (q_loc64_h:
+    [N, dqk] fp64 of that head; k_h / v_h: [Lkv, d] fp64)."""
+    out_o = np.zeros((q_loc64_h.shape[0], 1, v_h.shape[1]))
+    out_l = np.full((q_loc64_h.shape[0], 1), -np.inf)
+    for blk in chunks(rows, block):
+        o, l = ao.shard_attention(q_loc64_h[:, None], k_h[:, None], v_h[:, None], segs, 1, 1,
+                                  scale, kv_pos=kv_pos, rows=blk)
+        out_o[blk] = o[blk]
+        out_l[blk] = l[blk]
+    return out_o[:, 0], out_l[:, 0]
+
+
+def _gqa_prefill_all(w, rows_of):
+    """One prefill workload, every rank: the GPU output against the oracle on
+    rows_of(rank, oracle segments), all heads (heads x row blocks in a thread
+    pool)."""
     q, k, v = workloads.prefill_tensors(w, DEV)
-    q64, k64, v64 = f64(q), f64(k), f64(v)
     lens, pre = list(w.new_lens), list(w.prefix_lens)
+    G = w.hq // w.hkv
+    k64, v64 = f64(k), f64(v)
+    kh64 = [np.ascontiguousarray(k64[:, h]) for h in range(w.hkv)]
+    vh64 = [np.ascontiguousarray(v64[:, h]) for h in range(w.hkv)]
+    del k64, v64
     for r in range(w.cp_size):
         plan = cp.shard_plan(w.strategy, w.cp_size, r, lens, pre)
-        o, l = cp.attn_fwd(_local_q(q, plan), k, v, plan, w.scale)
+        q_loc = _local_q(q, plan)
+        o, l = cp.attn_fwd(q_loc, k, v, plan, w.scale)
         torch.cuda.synchronize()
-        segs = oracle_segments("zigzag", w.cp_size, r, lens, pre)
-        rows = range(plan.num_local) if r == 0 else sample_rows(segs, 48, seed=r)
-        toks = ix.rank_tokens("zigzag", w.cp_size, r, lens, pre)
-        ro, rl = ao.shard_attention(q64[[t.g for t in toks]], k64, v64, segs, w.hq, w.hkv,
-                                    w.scale, rows=rows)
+        segs = oracle_segments(w.strategy, w.cp_size, r, lens, pre)
+        rows = rows_of(r, segs)
+        q64 = f64(q_loc)
+        say(f"  rank {r}: {len(rows)} rows x {w.hq} heads, oracle ...")
+        tasks = [(h, blk) for h in range(w.hq) for blk in chunks(rows, 512)]
+        res = par_map(lambda t: _oracle_rows(q64[:, t[0]], kh64[t[0] // G], vh64[t[0] // G],
+                                             segs, w.scale, t[1]), tasks)
+        ro = np.zeros((plan.num_local, w.hq, w.dv))
+        rl = np.full((plan.num_local, w.hq), -np.inf)
+        for (h, blk), (oo, ll) in zip(tasks, res):
+            ro[blk, h] = oo[blk]
+            rl[blk, h] = ll[blk]
         compare(f64(o), f64(l), ro, rl, rows, "bf16", f"rank {r}")
     _zero_q_check(w, k, v, range(w.cp_size))
+
+
+def test_zigzag_t8192_p1024():
+    w = workloads.get("zigzag_t8192_p1024")
+    say(f"workload {w.name}: every row of every rank")
+    _gqa_prefill_all(w, lambda r, segs: [i for s in segs for i in range(s.q_begin, s.q_end)])
 
 
 def test_interleave_b12():
     w = workloads.get("interleave_b12")
     say(f"workload {w.name} lens={w.new_lens} prefix={w.prefix_lens}")
-    q, k, v = workloads.prefill_tensors(w, DEV)
-    q64, k64, v64 = f64(q), f64(k), f64(v)
-    lens, pre = list(w.new_lens), list(w.prefix_lens)
-    for r in range(w.cp_size):
-        plan = cp.shard_plan(w.strategy, w.cp_size, r, lens, pre)
-        o, l = cp.attn_fwd(_local_q(q, plan), k, v, plan, w.scale)
-        torch.cuda.synchronize()
-        segs = oracle_segments("interleave", w.cp_size, r, lens, pre)
-        rows = set(sample_rows(segs, 24, seed=10 + r))
-        for s in segs:                      # the two short requests: every row
-            if s.req < 2:
+    order = sorted(range(w.num_reqs), key=lambda b: -w.new_lens[b])
+    whole = {0, 1, order[0], order[1]}       # the two short and the two longest requests
+    say(f"  every row of requests {sorted(whole)}")
+
+    def rows_of(r, segs):
+        rows = set(sample_rows(segs, 256, seed=10 + r))
+        for s in segs:
+            if s.req in whole:
                 rows.update(range(s.q_begin, s.q_end))
-        rows = sorted(rows)
-        toks = ix.rank_tokens("interleave", w.cp_size, r, lens, pre)
-        ro, rl = ao.shard_attention(q64[[t.g for t in toks]], k64, v64, segs, w.hq, w.hkv,
-                                    w.scale, rows=rows)
-        compare(f64(o), f64(l), ro, rl, rows, "bf16", f"rank {r}")
-    _zero_q_check(w, k, v, range(w.cp_size))
+        return sorted(rows)
+    _gqa_prefill_all(w, rows_of)
 
 
-def _mla_rank(w, q, k, v, r, heads, n_rows):
-    lens, pre = list(w.new_lens), list(w.prefix_lens)
-    C = w.cp_size
+@pytest.fixture(scope="module")
+def mla_inputs():
+    w = workloads.get("zigzag_t131072_mla")
+    q, k, v = workloads.prefill_tensors(w, DEV)
+    return w, q, k, v, bf16_host(k), bf16_host(v)
+
+
+def _pair_segments(plan, n_keys):
+    return [cp.Segment(s.req, s.q_begin, s.q_end, s.pos_begin, s.pos_stride, 0, n_keys)
+            for s in plan.segments]
+
+
+@pytest.mark.parametrize("r", [0, 3, 7])
+def test_zigzag_t131072_mla(mla_inputs, r):
+    """Rank r of the 131072-token MLA prefill: the 8 ring partials (KV_j =
+    rank j's zigzag pair, masked by absolute key positions), their LSE
+    merge, the direct call over the full KV and, for rank 0, the 8 partials
+    accumulated in place (pass-Q accumulator, as the bench times it): every
+    one against the oracle on 256 seeded rows per block plus the block's
+    first and last row, all 128 heads."""
+    w, q, k, v, k_cpu, v_cpu = mla_inputs
+    lens, pre, C = list(w.new_lens), list(w.prefix_lens), w.cp_size
     plan = cp.shard_plan("zigzag", C, r, lens, pre)
     q_loc = _local_q(q, plan)
     n = plan.num_local
     segs_o = oracle_segments("zigzag", C, r, lens, pre)
-    rows = sample_rows(segs_o, n_rows, seed=40 + r)
-    mine = plan.global_idx.astype(np.int64)
-    hsel = torch.tensor(heads, device=DEV)
-    q_s = f64(q_loc[torch.tensor(rows, device=DEV)][:, hsel])        # [rows, nh, dqk]
-    # ring partials: KV_j = rank j's zigzag pair, masked by absolute positions
+    rows = sample_rows(segs_o, 256, seed=40 + r)
+    sel = torch.tensor(rows, device=DEV)
+    say(f"workload {w.name} rank {r}: {len(rows)} rows x {w.hq} heads")
+    pairs = [cp.shard_plan("zigzag", C, j, lens, pre).global_idx.astype(np.int64)
+             for j in range(C)]
     o_parts = torch.empty((C, n, w.hq, w.dv), device=DEV, dtype=torch.bfloat16)
     l_parts = torch.empty((C, n, w.hq), device=DEV, dtype=torch.float32)
+    acc_o = torch.full((n, w.hq, w.dv), 7.0, device=DEV, dtype=torch.bfloat16)
+    acc_l = torch.full((n, w.hq), -np.inf, device=DEV, dtype=torch.float32)
     for j in range(C):
-        say(f"  rank {r} ring partial {j}")
-        rows_j = cp.shard_plan("zigzag", C, j, lens, pre).global_idx.astype(np.int64)
-        idx = torch.from_numpy(rows_j).to(DEV)
-        kj, vj = k.index_select(0, idx), v.index_select(0, idx)
-        segs = [cp.Segment(s.req, s.q_begin, s.q_end, s.pos_begin, s.pos_stride, 0, len(rows_j))
-                for s in plan.segments]
-        cp.attn_fwd(q_loc, kj, vj, segs, w.scale, kv_pos=idx.to(torch.int32),
-                    o=o_parts[j], lse=l_parts[j])
-        torch.cuda.synchronize()
-        osegs = [ix.Segment(s.req, s.q_begin - 0, s.q_end, s.pos_begin, s.pos_stride, 0,
-                            len(rows_j)) for s in segs_o]
-        # oracle on the sampled rows / heads (row indices remapped to the sample)
-        sub_segs = _remap(osegs, rows)
-        ko, vo = f64(kj[:, hsel]), f64(vj[:, hsel])
-        ro, rl = ao.shard_attention(q_s, ko, vo, sub_segs, len(heads), len(heads), w.scale,
-                                    kv_pos=rows_j)
-        compare(f64(o_parts[j][torch.tensor(rows, device=DEV)][:, hsel]),
-                f64(l_parts[j][torch.tensor(rows, device=DEV)][:, hsel]),
-                ro, rl, range(len(rows)), "bf16", f"partial {j}")
+        idx = torch.from_numpy(pairs[j]).to(DEV)
+        kj, vj, pj = k.index_select(0, idx), v.index_select(0, idx), idx.to(torch.int32)
+        segs = _pair_segments(plan, len(pairs[j]))
+        cp.attn_fwd(q_loc, kj, vj, segs, w.scale, kv_pos=pj, o=o_parts[j], lse=l_parts[j])
+        if r == 0:
+            cp.attn_fwd(q_loc, kj, vj, segs, w.scale, kv_pos=pj, o=acc_o, lse=acc_l,
+                        accumulate=True)
         del kj, vj
     mo, ml = cp.lse_merge(o_parts, l_parts)
-    say(f"  rank {r} direct call over the full KV")
     do, dl = cp.attn_fwd(q_loc, k, v, plan, w.scale)
     torch.cuda.synchronize()
-    # merged vs direct on every row (both GPU)
-    err_o = float((mo.float() - do.float()).abs().max())
-    err_l = float((ml - dl).abs().max())
-    say(f"  merged vs direct, all rows: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
-    assert err_o <= 2e-2 and err_l <= 1e-3
-    ko, vo = f64(k[:, hsel]), f64(v[:, hsel])
-    ro, rl = ao.shard_attention(q_s, ko, vo, _remap(segs_o, rows), len(heads), len(heads),
-                                w.scale)
-    sel = torch.tensor(rows, device=DEV)
-    compare(f64(mo[sel][:, hsel]), f64(ml[sel][:, hsel]), ro, rl, range(len(rows)), "bf16",
-            "merged vs dense oracle")
-    compare(f64(do[sel][:, hsel]), f64(dl[sel][:, hsel]), ro, rl, range(len(rows)), "bf16",
-            "direct vs dense oracle")
-    del o_parts, l_parts
+    g_parts = (f64(o_parts[:, sel]), f64(l_parts[:, sel]))
+    got = {"merged": (f64(mo[sel]), f64(ml[sel])), "direct": (f64(do[sel]), f64(dl[sel]))}
+    if r == 0:
+        got["accumulated in place"] = (f64(acc_o[sel]), f64(acc_l[sel]))
+    del o_parts, l_parts, acc_o, acc_l, mo, ml, do, dl
+    q_s = f64(q_loc[sel])                                    # [rows, hq, dqk]
+    q_pos = plan.positions[rows].astype(np.int64)
+    # the sampled rows of each zigzag block: one oracle call per block, over
+    # the keys up to the block's last sampled position (later keys are
+    # invisible to all of them); one request, no prefix, so a key's position
+    # is its row in the full KV and its flattened index in a pair
+    blocks = []
+    for sg in segs_o:
+        ii = np.array([i for i, row in enumerate(rows) if sg.q_begin <= row < sg.q_end])
+        if len(ii):
+            blocks.append((ii, int(q_pos[ii].max()) + 1))
+    ro_d = np.zeros((len(rows), w.hq, w.dv))
+    rl_d = np.full((len(rows), w.hq), -np.inf)
+    ro_p = np.zeros((C, len(rows), w.hq, w.dv))
+    rl_p = np.full((C, len(rows), w.hq), -np.inf)
+
+    def head(h):
+        kh, vh = bf16_bits_f64(k_cpu[:, h]), bf16_bits_f64(v_cpu[:, h])
+        od = np.zeros((len(rows), w.dv))
+        ld = np.full(len(rows), -np.inf)
+        op = np.zeros((C, len(rows), w.dv))
+        lp = np.full((C, len(rows)), -np.inf)
+        for ii, kmax in blocks:
+            od[ii], ld[ii] = ao.attend(q_s[ii, h], kh[:kmax], vh[:kmax], q_pos[ii],
+                                       np.arange(kmax), w.scale)
+            for j in range(C):
+                kj = pairs[j][pairs[j] < kmax]
+                op[j, ii], lp[j, ii] = ao.attend(q_s[ii, h], kh[kj], vh[kj], q_pos[ii], kj,
+                                                 w.scale)
+        return od, ld, op, lp
+    for h, (od, ld, op, lp) in enumerate(par_map(head, range(w.hq))):
+        ro_d[:, h], rl_d[:, h] = od, ld
+        ro_p[:, :, h], rl_p[:, :, h] = op, lp
+    allr = range(len(rows))
+    for j in range(C):
+        compare(g_parts[0][j], g_parts[1][j], ro_p[j], rl_p[j], allr, "bf16", f"partial {j}")
+    for name, (go, gl) in got.items():
+        compare(go, gl, ro_d, rl_d, allr, "bf16", f"{name} vs dense oracle")
 
 
-def _remap(segs, rows):
-    """Segments restricted to the sampled rows, renumbered 0..len(rows)-1.
-    Each sampled row becomes a one-row segment with its own position."""
-    out = []
-    for i, r in enumerate(rows):
-        for s in segs:
-            if s.q_begin <= r < s.q_end:
-                pos = s.pos_begin + (r - s.q_begin) * s.pos_stride
-                out.append(ix.Segment(s.req, i, i + 1, pos, 1, s.kv_begin, s.kv_end))
-                break
-    assert len(out) == len(rows)
-    return out
-
-
-def test_zigzag_t131072_mla_ring_and_direct():
-    w = workloads.get("zigzag_t131072_mla")
-    say(f"workload {w.name}")
-    q, k, v = workloads.prefill_tensors(w, DEV)
-    # every 4th head and the last; 24 seeded rows per segment plus its first
-    # and last row (the fp64 oracle over 131072 keys bounds the sample)
-    heads = list(range(0, 128, 4)) + [127]
-    for r in (0, 7):
-        _mla_rank(w, q, k, v, r, heads, n_rows=24)
+def test_zigzag_t131072_mla_zero_query(mla_inputs):
+    w, q, k, v, _, _ = mla_inputs
     _zero_q_check(w, k, v, [0, 5])
