@@ -21,8 +21,9 @@ CP_ZIGZAG, CP_INTERLEAVE = 0, 1
 CP_F32, CP_BF16 = 0, 1
 
 EXPORTS = ("cp_shard_plan", "cp_restore_index", "cp_restore_apply", "cp_choose_pass",
-           "cp_ring_pad_len", "cp_attn_workspace_size", "cp_attn_fwd", "cp_lse_merge",
-           "cp_status_str", "cp_last_error", "cp_version")
+           "cp_ring_pad_len", "cp_attn_workspace_size", "cp_attn_fwd", "cp_attn_fwd_noalloc",
+           "cp_lse_merge", "cp_status_str", "cp_last_error", "cp_version")
+NOALLOC_SCRATCH_BYTES = 128 << 20   # CP_NOALLOC_SCRATCH_BYTES
 
 _STRATEGY = {"zigzag": CP_ZIGZAG, "interleave": CP_INTERLEAVE}
 
@@ -30,7 +31,7 @@ _STRATEGY = {"zigzag": CP_ZIGZAG, "interleave": CP_INTERLEAVE}
 class CpError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        detail = last_error() if status == CP_ERR_DEVICE else ""
+        detail = last_error() if status in (CP_ERR_DEVICE, CP_ERR_SMALL_BUFFER) else ""
         super().__init__(f"{what}: {status_str(status)} ({status}) {detail}".rstrip())
 
 
@@ -98,6 +99,8 @@ def _load():
     lib.cp_attn_workspace_size.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.cp_attn_fwd.restype = i32
     lib.cp_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), vp]
+    lib.cp_attn_fwd_noalloc.restype = i32
+    lib.cp_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), vp]
     lib.cp_lse_merge.restype = i32
     lib.cp_lse_merge.argtypes = [i32, i32, i32, i32, vp, i32, i64, vp, i64, vp, i32, vp, vp]
     lib.cp_status_str.restype = ctypes.c_char_p
@@ -333,6 +336,21 @@ def attn_fwd(q, k, v, segs, scale: float, causal: bool = True, kv_pos=None, o=No
     del keep
     if s != CP_OK:
         raise CpError(s, "cp_attn_fwd")
+    return o, lse
+
+
+def attn_fwd_noalloc(q, k, v, segs, scale: float, o, lse, causal: bool = True, kv_pos=None,
+                     stream=None, accumulate: bool = False, block_table=None,
+                     block_size: int = 0):
+    """cp_attn_fwd_noalloc: as attn_fwd with caller-given outputs, the
+    scratch taken from the library's static per-GPU array (no allocation
+    here or in the library).  Returns (o, lse)."""
+    a, keep = attn_args(q, k, v, segs, scale, o, lse, causal, kv_pos, None, accumulate,
+                        block_table, block_size)
+    s = _lib.cp_attn_fwd_noalloc(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream)))
+    del keep
+    if s != CP_OK:
+        raise CpError(s, "cp_attn_fwd_noalloc")
     return o, lse
 
 

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "cp_attn.h"
@@ -450,22 +451,24 @@ extern "C" cp_status cp_attn_workspace_size(const cp_attn_args *a, size_t *bytes
   return CP_OK;
 }
 
-extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
-  cp_status st = check_attn(a);
-  if (st != CP_OK) return st;
-  st = check_attn_buffers(a);
-  if (st != CP_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const AttnParams p = make_params(*a);
+namespace {
+
+// The attention call with its scratch in (ws, ws_bytes): the caller's
+// workspace (cp_attn_fwd) or the library's static scratch
+// (cp_attn_fwd_noalloc).  Arguments are already checked.
+cp_status attn_fwd_impl(const cp_attn_args *a, void *ws_ptr, size_t ws_bytes, hipStream_t s) {
+  AttnParams p = make_params(*a);
+  p.ws = ws_ptr;
+  p.ws_bytes = static_cast<int64_t>(ws_bytes);
   const Path path = pick_path(*a);
   (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
   if (path == Path::DecodeMla) {
     std::vector<DecodeLaunch> launches;
     const size_t need = plan_decode(*a, &launches);
-    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return CP_ERR_SMALL_BUFFER;
-    if (need > 0 && !aligned16(a->workspace)) return CP_ERR_ARG;
+    if (need > 0 && (!ws_ptr || ws_bytes < need)) return CP_ERR_SMALL_BUFFER;
+    if (need > 0 && !aligned16(ws_ptr)) return CP_ERR_ARG;
     for (DecodeLaunch &D : launches) {
-      D.ws_o = static_cast<float *>(a->workspace);
+      D.ws_o = static_cast<float *>(ws_ptr);
       D.ws_lse = D.ws_o + static_cast<size_t>(D.items) * D.nsplit * kDecodeHeadsPerBlock * 512;
       const hipError_t e = launch_attn_decode_mla(p, D, s);
       if (e != hipSuccess) return device_error(e);
@@ -482,9 +485,9 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
   // bf16: one int32 flag per workgroup, then (split calls) the partials
   const Bf16Plan P = plan_bf16(*a);
   const size_t need = P.bytes();
-  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return CP_ERR_SMALL_BUFFER;
-  if (need > 0 && !aligned16(a->workspace)) return CP_ERR_ARG;
-  char *ws = static_cast<char *>(a->workspace);
+  if (need > 0 && (!ws_ptr || ws_bytes < need)) return CP_ERR_SMALL_BUFFER;
+  if (need > 0 && !aligned16(ws_ptr)) return CP_ERR_ARG;
+  char *ws = static_cast<char *>(ws_ptr);
   AttnParams q = p;
   const int o_bf16 = a->o_dtype == CP_BF16 ? 1 : 0;
   const int64_t part_rows = P.part_rows * a->hq;  // (row, head) pairs per part
@@ -518,6 +521,70 @@ extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
     if (e != hipSuccess) return device_error(e);
   }
   return fill_empty_segments(a, s);
+}
+
+// Scratch of cp_attn_fwd_noalloc: one copy per GPU, in the code object's
+// static device memory (the runtime places it when the library's code is
+// loaded on that GPU; it stays until the process ends).  In host code the
+// name `scratch` is only a handle for hipGetSymbolAddress, never a device
+// address: kernels get the per-device address below.
+static __device__ __align__(256) unsigned char scratch[CP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch, looked up once per device with that
+// device current.
+cp_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_error(e);
+  if (dev < 0 || dev >= kMaxDevices) return CP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_error(e);
+    if (!ptr) return CP_ERR_DEVICE;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" cp_status cp_attn_fwd(const cp_attn_args *a, void *stream) {
+  cp_status st = check_attn(a);
+  if (st != CP_OK) return st;
+  st = check_attn_buffers(a);
+  if (st != CP_OK) return st;
+  return attn_fwd_impl(a, a->workspace, a->workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" cp_status cp_attn_fwd_noalloc(const cp_attn_args *a, void *stream) {
+  cp_status st = check_attn(a);
+  if (st != CP_OK) return st;
+  st = check_attn_buffers(a);
+  if (st != CP_OK) return st;
+  size_t need = 0;
+  const Path path = pick_path(*a);
+  if (path == Path::DecodeMla) need = plan_decode(*a, nullptr);
+  if (path == Path::Bf16Mfma) need = plan_bf16(*a).bytes();
+  if (need > CP_NOALLOC_SCRATCH_BYTES) {
+    snprintf(g_last_error, sizeof g_last_error,
+             "cp_attn_fwd_noalloc: the call needs %zu bytes of scratch, the library holds %zu",
+             need, static_cast<size_t>(CP_NOALLOC_SCRATCH_BYTES));
+    return CP_ERR_SMALL_BUFFER;
+  }
+  void *ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_current_device(&ws);
+    if (st != CP_OK) return st;
+  }
+  return attn_fwd_impl(a, ws, need > 0 ? CP_NOALLOC_SCRATCH_BYTES : 0,
+                       static_cast<hipStream_t>(stream));
 }
 
 extern "C" cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads,

@@ -25,10 +25,11 @@
  * Conventions shared by every call:
  *   - Ownership: the caller owns every buffer (host and device) and the
  *     stream.  The library allocates no device memory; scratch comes from a
- *     caller workspace whose size cp_attn_workspace_size reports.  What it
- *     keeps between calls is only the text of the calling thread's last
- *     device error (thread-local, read by cp_last_error); no result of a
- *     call depends on an earlier call.
+ *     caller workspace whose size cp_attn_workspace_size reports, or, for
+ *     cp_attn_fwd_noalloc, from a static device array inside the library.
+ *     Between calls it keeps only the text of the calling thread's last
+ *     error (thread-local, read by cp_last_error) and each GPU's address of
+ *     that static array; no result of a call depends on an earlier call.
  *   - Errors: every call returns a cp_status and never throws.  Arguments
  *     are checked on the host before anything is enqueued; on an error
  *     nothing is enqueued.  CP_ERR_SMALL_BUFFER still writes the required
@@ -294,6 +295,29 @@ cp_status cp_attn_workspace_size(const cp_attn_args *args, size_t *bytes);
 cp_status cp_attn_fwd(const cp_attn_args *args, void *stream);
 
 /*
+ * cp_attn_fwd_noalloc -- cp_attn_fwd for callers that cannot allocate device
+ * memory or hand over a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, same
+ * kernels, same results as cp_attn_fwd, except that args->workspace and
+ * args->workspace_bytes are ignored: the scratch cp_attn_workspace_size
+ * would report comes instead from a static device array inside the library,
+ * CP_NOALLOC_SCRATCH_BYTES bytes per GPU (placed when the library's code is
+ * loaded on that GPU, held until the process ends).  The call allocates no
+ * device memory (no hipMalloc / hipFree, no allocating library routine).
+ * Every call on one GPU shares that GPU's array and nothing in it needs to
+ * start at zero; two calls that overlap in time on the same GPU (other
+ * streams, other threads) race on it and give unspecified results: order
+ * them, e.g. on one stream.  Inputs and outputs are still the caller's.
+ * Errors: as cp_attn_fwd; CP_ERR_SMALL_BUFFER when the call needs more than
+ * CP_NOALLOC_SCRATCH_BYTES of scratch (cp_last_error then names both sizes;
+ * nothing is enqueued).  The first call on a GPU looks up that GPU's array
+ * address (hipGetSymbolAddress) with that GPU current; a failure there is
+ * CP_ERR_DEVICE.
+ */
+#define CP_NOALLOC_SCRATCH_BYTES (128u << 20)
+cp_status cp_attn_fwd_noalloc(const cp_attn_args *args, void *stream);
+
+/*
  * cp_lse_merge -- merge num_parts partial results of the same rows
  * ("What is Context Parallelism", section 3.6, read as the generalised
  * online softmax): per (row, head), with m = max_j L_j,
@@ -322,7 +346,8 @@ cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads,
 const char *cp_status_str(int32_t status);
 
 /* Name and description of the HIP error behind the calling thread's most
- * recent CP_ERR_DEVICE ("" if none yet).  Thread-local static storage, valid
+ * recent CP_ERR_DEVICE, or the sizes behind a CP_ERR_SMALL_BUFFER of
+ * cp_attn_fwd_noalloc ("" if none yet).  Thread-local static storage, valid
  * until the thread's next failing call. */
 const char *cp_last_error(void);
 

@@ -195,6 +195,27 @@ def _ws(**kw):
 ])
 def test_attn_arg_errors(kw, want):
     assert _fwd(**kw) == want
+    # the allocation-free entry point checks its arguments the same way,
+    # before it looks up any device scratch
+    a, keep = _args(**kw)
+    assert _lib._lib.cp_attn_fwd_noalloc(ctypes.byref(a), None) == want
+    del keep
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    # one long segment, 4 heads: few enough workgroups that the keys are split,
+    # fp32 partials of 16000 rows x 4 heads x 128 need more than the static
+    # scratch; the call must say so and enqueue nothing (no device is touched)
+    segs = (_lib.Segment * 1)(_lib.Segment(0, 0, 16000, (1 << 20) - 16000, 1, 0, 1 << 20))
+    kw = dict(num_q_rows=16000, num_kv_rows=1 << 20, hq=4, hkv=4, o_dtype=_lib.CP_F32,
+              k_row_stride=512, v_row_stride=512, num_segs=1, segs=segs)
+    st, need = _ws(**kw)
+    assert st == _lib.CP_OK and need > _lib.NOALLOC_SCRATCH_BYTES
+    a, keep = _args(**kw)
+    assert _lib._lib.cp_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.CP_ERR_SMALL_BUFFER
+    msg = _lib.last_error()
+    assert str(need) in msg and str(_lib.NOALLOC_SCRATCH_BYTES) in msg, msg
+    del keep
 
 
 def test_attn_segment_errors():
