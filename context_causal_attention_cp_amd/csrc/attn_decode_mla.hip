@@ -9,32 +9,33 @@
 // row: K = [c_KV (512) | k_pe (64)], and V is the first 512 columns of the
 // same row.
 //
-// One workgroup (8 waves) computes, for one query row and 128 query heads of
-// one KV head, the partial attention over one contiguous slice of the
-// shard's keys:
-//   * the heads are the MFMA N dimension, 16 per wave (v_mfma_f32_16x16x32_bf16);
-//     each wave keeps its 16 x 576 Q fragment in VGPRs and its 512 x 16 fp32
-//     O^T accumulator in AGPRs (two waves per SIMD);
-//   * key tiles of 32 latent rows (36 KiB) are copied HBM -> LDS with
-//     global_load_lds (no register staging), three tiles in flight;
-//   * S^T = K Q^T reads K rows from LDS; O^T += V^T P^T reads V^T from the
-//     same row-major tile with the transposing read ds_read_b64_tr_b16, so
-//     each latent row crosses HBM once and sits in LDS once;
-//   * the tile is XOR-swizzled in 16-byte chunks so that the row reads and
+// One workgroup (8 waves, two per SIMD) computes, for one query row and 128
+// query heads of one KV head, the partial attention over one contiguous
+// slice of the shard's keys, in tiles of 32 latent rows (36 KiB) copied
+// HBM -> LDS by buffer loads straight into LDS (no register staging):
+//   * main pass (attn_decode_px_kernel): wave w computes S^T = K Q^T for its
+//     16 heads (Q in registers, K rows read from LDS) and writes their
+//     softmax numerators P to LDS; after the tile's barrier every wave
+//     multiplies all 128 heads' P by its own 64 columns of V^T, read from the
+//     same row-major tile with the transposing ds_read_b64_tr_b16 (each
+//     latent row crosses HBM once and sits in LDS once).  Every head's
+//     softmax reference is the max of its first tile; a slice whose row sums
+//     outgrow 2^64 (or whose accumulators are not finite) is flagged;
+//   * exact pass (attn_decode_mla_kernel): recomputes only the flagged
+//     slices, each wave with 16 heads' whole 512 x 16 O^T and a reference
+//     that moves (with a rescale) when a tile outgrows it by 2^8;
+//   * the tiles are XOR-swizzled in 16-byte chunks so that the row reads and
 //     the transposing reads are free of bank conflicts under gfx950's lane
 //     grouping of 16- and 8-byte LDS reads;
-//   * each lane keeps the softmax reference max of its head; the waves only
-//     exchange row maxima (and rescale the accumulator) when some lane's
-//     tile max exceeds the reference by more than 2^8;
 // and writes the slice's normalised partial (O_s, LSE_s) to the workspace.
 //
 // Paged KV (the cache of a rank that holds whole blocks of tokens, section
-// 2.2's block interleave): the slice's block ids are staged in LDS once; a
-// 32-row tile never crosses a block (blocks are multiples of 32 rows and
-// segments start on a tile), so each tile gets its own buffer resource at
-// its block's pool row and the per-lane offsets stay those of a
-// contiguous tile.
-// A second kernel merges the slices of each (row, head) by LSE.
+// 2.2's block interleave): a 32-row tile never crosses a block (blocks are
+// multiples of 32 rows and segments start on a tile), so each tile gets its
+// own buffer resource at its block's pool row and the per-lane offsets stay
+// those of a contiguous tile (the main pass reads the tile's block id from
+// the table; the exact pass stages the slice's ids in LDS once).
+// A third kernel merges the slices of each (row, head) by LSE.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -146,9 +147,14 @@ __device__ inline void decode_item(const DecodeLaunch &D, int item, int &si, int
   row = rem / D.hkv;
 }
 
+// The exact pass: recomputes the slices the main pass (attn_decode_px_kernel)
+// flagged, with a per-head reference max that moves (and rescales the
+// accumulator) whenever a tile outgrows it by more than 2^8.  Each wave keeps
+// 16 heads' Q and their whole 512 x 16 O^T, so no state crosses waves.
 template <bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
+  if (D.ws_flags[blockIdx.x] == 0) return;  // the main pass wrote this slice
   // key tiles, then (paged) the slice's block ids, in ONE LDS object: with a
   // second LDS variable the waitcnt pass can no longer tell the tile reads
   // from the in-flight LDS-DMA writes and drains them (vmcnt(0)) every tile
@@ -424,6 +430,373 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
         make_float4(oacc[b][0] * inv, oacc[b][1] * inv, oacc[b][2] * inv, oacc[b][3] * inv);
 }
 
+// ---------------------------------------------------------------------------
+// Main pass: the same slice and tiles, with the products split across the
+// waves by what each operand is shared by.  Wave w computes S^T = K Q^T for
+// its 16 heads (Q stays in its registers, K rows are read from LDS), takes
+// the softmax numerators P of those heads, and writes them to LDS; after the
+// tile's barrier every wave multiplies ALL 128 heads' P by its own 64 columns
+// of V^T (O^T[64w .. 64w + 63][all heads] lives in its accumulators).  Per
+// tile and CU that is 8 x 8 transposing reads of V^T instead of 8 x 64, and
+// 8 x 8 row reads of P: about 420 LDS read instructions instead of 800, for
+// the same 544 products.
+//   * one barrier per tile: iteration t runs PV of tile t-1 and S of tile t,
+//     so P is double-buffered (2 x 8 KiB) and four stages of 36 KiB hold the
+//     tiles being read (t-1: V, t: K) and the two in flight (t+1, t+2);
+//   * every head's softmax reference is the max of its first tile and never
+//     moves, so no wave ever rescales another wave's accumulators; a slice in
+//     which some row sum ends above 2^64 (or any accumulator is not finite) is
+//     flagged and recomputed by the exact pass (attn_decode_mla_kernel).
+// LDS of P: 16-byte units, unit (g * 128 + head) holds the eight numerators
+// of `head` that lane group g of an MFMA operand carries (keys 4g..4g+3 and
+// 16+4g..16+4g+3): the S owner writes its lane's eight at once, and a 16-lane
+// run of a reader covers 16 consecutive units (one 256-byte bank row), free of
+// bank conflicts under gfx950's lane groups for 16-byte reads.
+constexpr int NBUF_X = 4;                   // main pass: LDS stages
+constexpr int PB_UNITS = 4 * HT;            // one P buffer, 16-byte units (8 KiB)
+constexpr int DBW = DV / NW / 16;           // 16-row dv blocks of O^T per wave (4)
+constexpr int HBK = HT / 16;                // 16-head blocks (8)
+constexpr float kMaxSum = 18446744073709551616.0f;  // 2^64: largest accepted row sum
+static_assert((NBUF_X * TILE_CH + 2 * PB_UNITS) * 16 <= 160 * 1024, "LDS");
+
+// x, hidden from the optimiser (keeps per-lane values that are cheap to
+// rebuild from being hoisted and kept live across the loop).  A __device__
+// function: inline asm with a VGPR constraint inside a kernel's lambda is
+// also checked for the host, where the constraint does not exist, and the
+// kernel's host-side launch stub then silently disappears.
+__device__ inline int opaque_lane(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// byte offset of lane ln's 16-byte chunk in DMA instruction wi of a tile
+// (rows k_rs elements apart, chunks swizzled as in the LDS tile)
+__device__ inline uint32_t dma_lane_offset(int wi, int ln, int k_rs) {
+  const int slot = wi * 64 + ln;
+  const int key = slot / KCH, cs = slot % KCH;
+  return (uint32_t)(key * k_rs + (cs ^ swz(key)) * 8) * 2u;
+}
+
+__device__ inline uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+// 16-byte LDS read / write through inline asm (compiler-visible LDS accesses
+// in the loop would make the waitcnt pass drain the DMA queue); results are
+// consumed only after an explicit lgkmcnt wait that names them
+__device__ inline u32x4 lds_read_b128(const void *p) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+  return r;
+}
+__device__ inline void lds_write_b128(void *p, const u32x4 &v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+// PV step: the eight P reads and the first V^T block's two reads complete
+// (the next block's two may still be pending); then one V^T block at a time
+__device__ inline void lds_wait_p8_v(u32x4 (&pr)[HBK], u32x2 (&v)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(2)"
+               : "+v"(pr[0]), "+v"(pr[1]), "+v"(pr[2]), "+v"(pr[3]), "+v"(pr[4]), "+v"(pr[5]),
+                 "+v"(pr[6]), "+v"(pr[7]), "+v"(v[0]), "+v"(v[1]));
+}
+template <int LATER>
+__device__ inline void lds_wait_v(u32x2 (&v)[2]) {
+  if constexpr (LATER == 2) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(v[0]), "+v"(v[1]));
+  else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]));
+}
+// vmcnt(N) and lgkmcnt(0) in one wait (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vm_lgkm0() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+template <bool PAGED>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+void attn_decode_px_kernel(const AttnParams p, const DecodeLaunch D) {
+  __shared__ __attribute__((aligned(1024))) u32x4 lds[NBUF_X * TILE_CH + 2 * PB_UNITS];
+  char *const pbuf = (char *)(lds + NBUF_X * TILE_CH);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int item = blockIdx.x / D.nsplit, split = blockIdx.x % D.nsplit;
+  if (item >= D.items) return;
+  int si, row, kvh, ht;
+  decode_item(D, item, si, row, kvh, ht);
+  const SegDesc sd = D.s[si];
+  const int G = p.hq / p.hkv;
+  const int hl = ht * HT + w * HW + n;           // this lane's S head within the KV group
+  const bool hvalid = hl < G;
+  const int h = kvh * G + hl;
+  const int64_t qrow = (int64_t)sd.q_begin + row;
+  const int qpos = sd.pos_begin + row * sd.pos_stride;
+
+  // this workgroup's key slice (as in the exact pass)
+  const int chunk = ((sd.kv_len + D.nsplit - 1) / D.nsplit + BN - 1) / BN * BN;
+  const int k_lo = min(sd.kv_len, split * chunk);
+  const int k_hi = min(sd.kv_len, k_lo + chunk);
+  const int64_t pos_base =
+      PAGED ? (int64_t)sd.req * p.bt_stride * p.block_size + sd.kv_begin : (int64_t)sd.kv_begin;
+  const int32_t *kvp = p.kv_pos ? p.kv_pos + pos_base : nullptr;
+  auto key_pos = [&](int j) -> int { return kvp ? kvp[j] : j; };
+  int k_vis = k_hi;
+  if (p.causal && k_hi > k_lo && key_pos(k_hi - 1) > qpos) {
+    int lo = k_lo, hi = k_hi;  // first key with position > qpos
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (key_pos(mid) <= qpos) lo = mid + 1; else hi = mid;
+    }
+    k_vis = lo;
+  }
+  const int ntiles = (k_vis - k_lo + BN - 1) / BN;
+
+  // Q fragments: B operand of S^T = K Q^T (n = head, k = d: 8 per lane group)
+  bf16x8 qf[QS];
+  {
+    const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)h * p.q_hs + 8 * g;
+#pragma unroll
+    for (int st = 0; st < QS; ++st) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (hvalid && ntiles > 0) x = *(const u32x4 *)(qp + 32 * st);
+      qf[st] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // LDS DMA: waves 0-3 issue 5 and waves 4-7 issue 4 of the 36 instructions
+  // of a tile, through a buffer resource that ends at the slice end (rows
+  // past k_hi read as zeros)
+  const __bf16 *kbase = (const __bf16 *)p.k + (int64_t)sd.kv_begin * p.k_rs + (int64_t)kvh * p.k_hs;
+  const int wi0 = w < 4 ? 5 * w : 20 + 4 * (w - 4);
+  const int wn = w < 4 ? 5 : 4;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)kbase, (short)0, (int)((int64_t)k_hi * p.k_rs * 2), 0x00020000);
+  const int x_lo = sd.kv_begin + k_lo;  // paged: first logical row of the slice
+  auto tile_rsrc = [&](int t, uint32_t &row0) -> __amdgpu_buffer_rsrc_t {
+    if (!PAGED) {
+      row0 = (uint32_t)((k_lo + t * BN) * p.k_rs) * 2u;
+      return krsrc;
+    }
+    // the tile's 32 rows sit in one block (clamped into the pool)
+    const int x0 = x_lo + t * BN;
+    int b = p.block_table[(int64_t)sd.req * p.bt_stride + x0 / p.block_size];
+    b = __builtin_amdgcn_readfirstlane(min(max(b, 0), p.pool_blocks - 1));
+    const int64_t prow = (int64_t)b * p.block_size + x0 % p.block_size;
+    const int rows = min(BN, k_hi - (k_lo + t * BN));
+    row0 = 0u;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const __bf16 *)p.k + prow * p.k_rs + (int64_t)kvh * p.k_hs), (short)0,
+        (int)(rows * p.k_rs * 2), 0x00020000);
+  };
+  // per-lane DMA byte offsets: the four every wave issues are kept; the fifth
+  // (waves 0-3 only) is rebuilt at each issue from an opaque copy of the lane
+  // id -- kept live it was the register the allocator spilled, and reloading
+  // it made the compiler wait for every DMA in flight (vmcnt(0)) each tile
+  uint32_t dma_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma_off[i] = dma_lane_offset(wi0 + i, lane, (int)p.k_rs);
+  auto issue = [&](int t) {
+    uint32_t row0;
+    const __amdgpu_buffer_rsrc_t trsrc = tile_rsrc(t, row0);
+    u32x4 *dst = lds + (t % NBUF_X) * TILE_CH;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          trsrc, (__attribute__((address_space(3))) void *)(dst + (wi0 + i) * 64), 16,
+          row0 + dma_off[i], 0, 0, 0);
+    if (wn == 5) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          trsrc, (__attribute__((address_space(3))) void *)(dst + (wi0 + 4) * 64), 16,
+          row0 + dma_lane_offset(wi0 + 4, opaque_lane(lane), (int)p.k_rs), 0, 0, 0);
+    }
+  };
+
+  // O^T[64w + 16db + 4g + i][16hb + n] in oacc[hb][db][i]
+  f32x4 oacc[HBK][DBW];
+#pragma unroll
+  for (int hb = 0; hb < HBK; ++hb)
+#pragma unroll
+    for (int db = 0; db < DBW; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[hb][db][i] = 0.f;
+  float m_ref = 0.f;   // reference max of this lane's S head (log2 units), fixed at tile 0
+  float l_run = 0.f;   // this lane's partial row sum
+  const float sl2 = p.scale_log2;
+
+  constexpr int kRow16 = 16 * KCH * 16;
+  auto lds_bases = [&](int (&qk_base)[2], int (&tr_base)[4]) {
+    const int ln = opaque_lane(lane);
+    const int nn = ln & 15, gg = ln >> 4;
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) qk_base[odd] = 16 * (nn * KCH + ((4 * odd + gg) ^ swz(nn)));
+    const int key = 4 * gg + (nn >> 2);
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4)
+      tr_base[b4] = 16 * (key * KCH + ((2 * b4 + ((nn & 3) >> 1)) ^ swz(key))) + 8 * (nn & 1);
+  };
+  // P units of this lane (rebuilt where used from an opaque copy of the lane
+  // id, like the tile bases, instead of being kept live across the loop):
+  // the reader's unit for head block 0 (+ 256 bytes per block), the S owner's
+  auto p_units = [&](int &rd, int &wr) {
+    const int ln = opaque_lane(lane);
+    rd = ((ln >> 4) * HT + (ln & 15)) * 16;
+    wr = rd + w * HW * 16;
+  };
+
+  // O^T += V^T P^T of tile u: this wave's 64 dv columns, all 128 heads.  All
+  // eight P reads go out at once (one LDS latency for the step), then the
+  // V^T fragments stream one dv block ahead of its eight products.
+  auto pv = [&](int u) {
+    const char *tile = (const char *)(lds + (u % NBUF_X) * TILE_CH);
+    int p_rd, p_wr;
+    p_units(p_rd, p_wr);
+    const char *pb = pbuf + (u & 1) * PB_UNITS * 16 + p_rd;
+    int qk_base[2], tr_base[4];
+    lds_bases(qk_base, tr_base);
+    u32x4 pr[HBK];
+#pragma unroll
+    for (int hb = 0; hb < HBK; ++hb) pr[hb] = lds_read_b128(pb + 256 * hb);
+    u32x2 vr[2][2];
+    auto vread = [&](int db, u32x2 (&r)[2]) {
+      r[0] = lds_read_tr16(tile + tr_base[db] + 128 * w);
+      r[1] = lds_read_tr16(tile + tr_base[db] + kRow16 + 128 * w);
+    };
+    vread(0, vr[0]);
+    vread(1, vr[1]);
+    lds_wait_p8_v(pr, vr[0]);     // the P reads and V of block 0 (block 1's two may pend)
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) {
+      u32x2 (&cur)[2] = vr[db & 1];
+      if (db > 0) {
+        if (db + 1 < DBW) lds_wait_v<2>(cur);
+        else lds_wait_v<0>(cur);
+      }
+      const u32x4 av = {cur[0][0], cur[0][1], cur[1][0], cur[1][1]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+      for (int hb = 0; hb < HBK; ++hb)
+        oacc[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pr[hb]),
+                                                               oacc[hb][db], 0, 0, 0);
+      if (db + 2 < DBW) vread(db + 2, cur);
+    }
+  };
+
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  for (int t = 0; t < ntiles; ++t) {
+    // tile t has landed (only tile t + 1 may still be in flight) and this
+    // wave's P(t - 1) is written; after the barrier every wave has both
+    if (t + 1 < ntiles) {
+      if (w < 4) wait_vm_lgkm0<5>(); else wait_vm_lgkm0<4>();
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (t + 2 < ntiles) issue(t + 2);
+    if (t > 0) pv(t - 1);
+    // ---- S^T = K Q^T of tile t for this wave's heads, their numerators
+    // against the fixed reference, written to P buffer t & 1
+    // a scheduling region of its own: the products of the PV step above
+    // would otherwise take the first slots of the pattern below
+    __builtin_amdgcn_sched_barrier(0);
+    const char *tile = (const char *)(lds + (t % NBUF_X) * TILE_CH);
+    const int j0 = k_lo + t * BN;
+    int qk_base[2], tr_base[4];
+    lds_bases(qk_base, tr_base);
+    // ---- S^T = K Q^T : two 16-key blocks x 16 heads
+    // the two key blocks' accumulation chains alternate, so consecutive
+    // products never depend on each other
+    f32x4 sc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[mb][i] = 0.f;
+#pragma unroll
+    for (int st = 0; st < QS; ++st)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a =
+            *(const bf16x8 *)(tile + qk_base[st & 1] + kRow16 * mb + 128 * (st >> 1));
+        sc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], sc[mb], 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads ahead
+#pragma unroll
+    for (int i = 0; i < 2 * QS - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    // ---- mask (keys at or past k_vis), numerators against the fixed reference
+    const bool full = j0 + BN <= k_vis;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float u = sc[mb][i] * sl2;
+        if (!full) u = (j0 + 16 * mb + 4 * g + i < k_vis) ? u : -INFINITY;
+        sc[mb][i] = u;
+        mx = fmaxf(mx, u);
+      }
+    if (t == 0) m_ref = max_groups(mx);   // tile 0 holds a visible key of every head
+    u32x4 pk;
+    float ls = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[mb][0] - m_ref), p1 = __builtin_amdgcn_exp2f(sc[mb][1] - m_ref);
+      const float p2 = __builtin_amdgcn_exp2f(sc[mb][2] - m_ref), p3 = __builtin_amdgcn_exp2f(sc[mb][3] - m_ref);
+      ls += (p0 + p1) + (p2 + p3);
+      pk[2 * mb] = pack_bf16(p0, p1);
+      pk[2 * mb + 1] = pack_bf16(p2, p3);
+    }
+    l_run += ls;
+    int p_rd, p_wr;
+    p_units(p_rd, p_wr);
+    lds_write_b128(pbuf + (t & 1) * PB_UNITS * 16 + p_wr, pk);
+  }
+  if (ntiles > 0) {
+    wait_vm_lgkm0<0>();             // P of the last tile written
+    __builtin_amdgcn_s_barrier();
+    pv(ntiles - 1);
+  }
+
+  // ---- flags: a row sum above 2^64 (some numerator may have left the
+  // range the fixed reference keeps exact) or a non-finite accumulator
+  const float l_tot = sum_groups(l_run);
+  bool bad = !(l_tot <= kMaxSum);
+#pragma unroll
+  for (int hb = 0; hb < HBK; ++hb)
+#pragma unroll
+    for (int db = 0; db < DBW; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bad = bad || !__builtin_isfinite(oacc[hb][db][i]);
+  const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  // row sums of all heads and the waves' flags through the P buffer that no
+  // wave reads any more (the last tile's P is in the other one)
+  float *xch = (float *)(pbuf + (ntiles & 1) * PB_UNITS * 16);
+  if (g == 0) xch[w * HW + n] = l_tot;
+  if (lane == 0) ((int *)xch)[HT + w] = wave_bad ? 1 : 0;
+  __syncthreads();
+  int flagged = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) flagged |= ((const int *)xch)[HT + i];
+  if (tid == 0) D.ws_flags[blockIdx.x] = flagged;
+  if (flagged) return;  // the exact pass writes this slice
+  const int64_t part = (int64_t)item * D.nsplit + split;
+  if (g == 0 && hvalid)
+    D.ws_lse[part * HT + w * HW + n] =
+        l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int hb = 0; hb < HBK; ++hb) {
+    const float lt = xch[16 * hb + n];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float *wo = D.ws_o + (part * HT + 16 * hb + n) * DV + 64 * w + 4 * g;
+#pragma unroll
+    for (int db = 0; db < DBW; ++db)
+      *(float4 *)(wo + 16 * db) = make_float4(oacc[hb][db][0] * inv, oacc[hb][db][1] * inv,
+                                              oacc[hb][db][2] * inv, oacc[hb][db][3] * inv);
+  }
+}
+
 // Merge of the slices of one (row, head): one wave per (item, head), 8 dv
 // elements per lane, LSE merge over the slices.
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const AttnParams p,
@@ -505,12 +878,16 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const AttnPara
 
 hipError_t launch_attn_decode_mla(const AttnParams &p, const DecodeLaunch &D, hipStream_t stream) {
   if (D.items <= 0) return hipSuccess;
-  if (p.block_table)
-    hipLaunchKernelGGL(attn_decode_mla_kernel<true>, dim3((unsigned)(D.items * D.nsplit)),
-                       dim3(NT), 0, stream, p, D);
-  else
-    hipLaunchKernelGGL(attn_decode_mla_kernel<false>, dim3((unsigned)(D.items * D.nsplit)),
-                       dim3(NT), 0, stream, p, D);
+  const dim3 grid((unsigned)(D.items * D.nsplit));
+  // main pass (flags the slices it cannot keep exact), then the exact pass
+  // over the flagged slices only
+  if (p.block_table) {
+    hipLaunchKernelGGL(attn_decode_px_kernel<true>, grid, dim3(NT), 0, stream, p, D);
+    hipLaunchKernelGGL(attn_decode_mla_kernel<true>, grid, dim3(NT), 0, stream, p, D);
+  } else {
+    hipLaunchKernelGGL(attn_decode_px_kernel<false>, grid, dim3(NT), 0, stream, p, D);
+    hipLaunchKernelGGL(attn_decode_mla_kernel<false>, grid, dim3(NT), 0, stream, p, D);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t waves = (int64_t)D.items * HT;

@@ -368,8 +368,8 @@ size_t plan_decode(const cp_attn_args &a, std::vector<DecodeLaunch> *out) {
     D.nsplit = nsplit;
     D.htiles = htiles;
     D.hkv = a.hkv;
-    ws = std::max(ws, static_cast<size_t>(items) * nsplit * kDecodeHeadsPerBlock *
-                          (512 + 1) * sizeof(float));
+    ws = std::max(ws, static_cast<size_t>(items) * nsplit *
+                          (kDecodeHeadsPerBlock * (512 + 1) * sizeof(float) + sizeof(int32_t)));
     if (out) out->push_back(D);
   }
   return ws;
@@ -470,6 +470,8 @@ cp_status attn_fwd_impl(const cp_attn_args *a, void *ws_ptr, size_t ws_bytes, hi
     for (DecodeLaunch &D : launches) {
       D.ws_o = static_cast<float *>(ws_ptr);
       D.ws_lse = D.ws_o + static_cast<size_t>(D.items) * D.nsplit * kDecodeHeadsPerBlock * 512;
+      D.ws_flags = reinterpret_cast<int32_t *>(
+          D.ws_lse + static_cast<size_t>(D.items) * D.nsplit * kDecodeHeadsPerBlock);
       const hipError_t e = launch_attn_decode_mla(p, D, s);
       if (e != hipSuccess) return device_error(e);
     }

@@ -68,8 +68,9 @@ struct AttnParams {
 // block of kDecodeHeadsPerBlock query heads, key slice).  Segments travel in
 // the kernel arguments; tile_begin counts work items (q_len * hkv * htiles
 // per segment).  Slice partials go to the workspace:
-//   ws_o   fp32 [items][nsplit][kDecodeHeadsPerBlock][512]
-//   ws_lse fp32 [items][nsplit][kDecodeHeadsPerBlock]
+//   ws_o     fp32 [items][nsplit][kDecodeHeadsPerBlock][512]
+//   ws_lse   fp32 [items][nsplit][kDecodeHeadsPerBlock]
+//   ws_flags int32 [items][nsplit]  (main pass: 1 = recompute in the exact pass)
 constexpr int kDecodeHeadsPerBlock = 128;
 // paged KV: block ids of one key slice staged in LDS
 constexpr int kDecodeMaxSliceBlocks = 1024;
@@ -83,6 +84,7 @@ struct DecodeLaunch {
   int32_t reserved;
   float *ws_o;
   float *ws_lse;
+  int32_t *ws_flags;
   SegDesc s[kMaxLaunchSegs];
 };
 

@@ -153,6 +153,36 @@ def test_decode_reference_growth(val):
         compare(f64(o[b]), f64(l[b]), ro, rl, range(hq), "bf16", f"req {b}")
 
 
+def test_decode_huge_values_overflow_guard():
+    """A key whose score is 2^59.9 above the first tile's (q is zero on the
+    512 latent columns and one on the 64 rope columns, so the score comes
+    from the rope part alone) while its latent columns -- its V row -- are
+    near 2^70: the main pass's numerator times V leaves the fp32 range
+    although the exact output is finite.  The slice must be flagged and
+    recomputed; O is compared after scaling by 2^-70 (linear in V)."""
+    B, ctx, hq, big = 2, 3000, 128, 2.0 ** 70
+    g = torch.Generator(device=DEV)
+    g.manual_seed(777)
+    q = torch.zeros((B, hq, DQK), device=DEV, dtype=torch.bfloat16)
+    q[:, :, DV:] = 1.0
+    kv = torch.randn((B, ctx, DQK), generator=g, device=DEV)
+    kv[:, :, DV:] = 0.0
+    kv[0, 2000, DV:] = 0.6484375          # 64 x 0.6484375 x log2(e) = 59.87
+    kv[0, 2000, :DV] *= big
+    kv[1, 40, DV:] = 0.6484375
+    kv[1, 40, :DV] *= big
+    kv = kv.to(torch.bfloat16)
+    say("decode huge values")
+    outs = _run_shards(q, kv, 1, 1.0)
+    torch.cuda.synchronize()
+    o, l = outs[0]
+    assert bool(torch.isfinite(o.float()).all()), "non-finite O"
+    q64, kv64 = f64(q), f64(kv)
+    for b in range(B):
+        ro, rl = _oracle_shard(q64, kv64, b, 0, 1, 1.0, ctx)
+        compare(f64(o[b]) / big, f64(l[b]), ro / big, rl, range(hq), "bf16", f"req {b} (O / 2^70)")
+
+
 def test_decode_accumulate_in_place():
     """The W shard partials merged into a running (O, LSE) by the decode
     combine (accumulate=1) instead of a separate merge."""
