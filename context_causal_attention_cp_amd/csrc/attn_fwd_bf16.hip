@@ -36,6 +36,15 @@
 // Work mapping: all workgroups of one KV head go to one XCD (id mod 8) so the
 // ones streaming the same K/V share that XCD's L2; inside a head the
 // heaviest tiles (longest causal extent) start first.
+//
+// For qk 192 (the MLA shape) the main pass of 256-row workgroups runs as
+// attn_fwd_bf16_split_kernel instead: 8 waves, two per SIMD, the score waves
+// holding Q and the output waves holding O of the same 64 rows, with the
+// probabilities handed over through LDS.  A single wave per SIMD issues its
+// products, exponentials, DMA descriptors and waits in order and leaves the
+// matrix core idle whenever it stalls; with two waves per SIMD the other
+// wave's products fill those gaps.  Same arithmetic in the same order: the
+// results are bitwise those of the one-wave kernel.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -689,11 +698,484 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   }
 }
 
+// wait until this wave's own DMA of a tile is complete (at most `later` later
+// tiles of PER instructions each still in flight) and its LDS operations are
+// done (the probabilities it wrote, the fragments it read)
+template <int N>
+__device__ inline void wait_vm_lgkm0() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+template <int PER, int MAXL>
+__device__ inline void wait_later_lgkm0(int later) {
+  if constexpr (MAXL >= 5) if (later >= 5) { wait_vm_lgkm0<5 * PER>(); return; }
+  if constexpr (MAXL >= 4) if (later == 4) { wait_vm_lgkm0<4 * PER>(); return; }
+  if constexpr (MAXL >= 3) if (later == 3) { wait_vm_lgkm0<3 * PER>(); return; }
+  if constexpr (MAXL >= 2) if (later == 2) { wait_vm_lgkm0<2 * PER>(); return; }
+  if constexpr (MAXL >= 1) if (later == 1) { wait_vm_lgkm0<PER>(); return; }
+  wait_vm_lgkm0<0>();
+}
+
+// This lane's index, recomputed where it is used (2 VALU): an asm barrier on
+// the input keeps the compiler from hoisting it out of the loop and holding
+// it (or spilling it) across the loop.
+__device__ inline uint32_t lane_id_here() {
+  uint32_t z = 0;
+  asm volatile("" : "+v"(z));
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z));
+}
+
+// Stages of the split-role main pass: the probabilities of a tile take a
+// double buffer of 2 x 4 waves x 4 KiB next to the K/V stages.
+template <int DQK, int DV>
+struct SplitCfg {
+  using C = Cfg<DQK, DV>;
+  static constexpr int PBYTES = 2 * 4 * 4096;
+  static constexpr int NBUF_FIT = (160 * 1024 - PBYTES - 3 * 1024) / (C::STAGE * 16);
+  static constexpr int NBUF = NBUF_FIT < 8 ? NBUF_FIT : 8;
+  // a stage is read in iterations i (K) and i + 2 (V)
+  static constexpr int PREF = NBUF - 3;
+  static_assert(PREF >= 2, "stages");
+};
+
+// Main pass of 256-row workgroups with split roles: 8 waves, two per SIMD.
+// Waves 0-3 ("score waves") hold Q of 64 rows each and compute the scores and
+// the probabilities; waves 4-7 ("output waves") hold the O accumulators of the
+// same rows.  Score wave s and output wave 4 + s share a SIMD, so one wave's
+// exponentials run on the VALU while the other's products run on the matrix
+// core, and no wave keeps both Q and O (which would not fit the 256 registers
+// a wave has at two waves per SIMD for qk 192).  Per iteration i (one barrier):
+//   score waves:  S(i) = K(i) Q^T, interleaved with the exponentials of
+//                 S(i - 1), which go to LDS as P(i - 1) (bf16, already in the
+//                 B-operand layout of the PV product: lane l of the output
+//                 wave reads what lane l of its score wave wrote);
+//   output waves: O^T += V(i - 2)^T P(i - 2)^T.
+// The arithmetic and its order are those of attn_fwd_bf16_kernel<.., 2, false>
+// (same scores, same bf16 probabilities, same row sums, same product order),
+// so outputs, log-sum-exps and flags are bitwise the same; the exact pass of
+// that kernel recomputes the flagged workgroups.
+template <int DQK, int DV>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
+  using C = Cfg<DQK, DV>;
+  using SC = SplitCfg<DQK, DV>;
+  constexpr int RB = 2, RW = 64, BM = 256;
+  constexpr int KCH = C::KCH, VCH = C::VCH, KS = C::KS, OB = C::OB;
+  constexpr int BN = C::BN, NBUF = SC::NBUF, PREF = SC::PREF;
+  __shared__ __attribute__((aligned(1024))) u32x4 sm[NBUF][C::STAGE];
+  __shared__ __attribute__((aligned(16))) u32x4 pbuf[2][4][2 * RB][64];  // [i&1][wave][rb,c][lane]
+  __shared__ float s_l[BM], s_m[BM];  // row sums and references, score -> output waves
+  __shared__ float s_lse[4 * 32];
+  __shared__ int s_flag;
+  int32_t *const flags = (int32_t *)p.ws;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool score = w < 4;
+  const int s = w & 3;  // the 64-row slice of this wave
+  const int lane = tid & 63, n = lane & 31, hf = lane >> 5;
+
+  int tile_order, h;
+  map_work(blockIdx.x, L.num_tiles, p.hq, p.hkv, tile_order, h);
+  if (tile_order >= L.num_tiles) return;
+  if (tid == 0) s_flag = 0;
+  __syncthreads();
+  const SegDesc sd = L.s[find_seg(L, tile_order)];
+  const int ntile_q = (sd.q_len + BM - 1) / BM;
+  const int tq = ntile_q - 1 - (tile_order - sd.tile_begin);
+  const int row0 = tq * BM;
+  const int rows_here = min(BM, sd.q_len - row0);
+  const int kvh = h / (p.hq / p.hkv);
+
+  int qpos[RB];
+  bool valid[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = s * RW + rb * 32 + n;
+    valid[rb] = rr < rows_here;
+    qpos[rb] = valid[rb] ? sd.pos_begin + (row0 + rr) * sd.pos_stride : kNoPos;
+  }
+  const int nvalid_w = max(0, min(RW, rows_here - s * RW));
+  const int qmin_w = nvalid_w ? sd.pos_begin + (row0 + s * RW) * sd.pos_stride : kNoPos;
+  const int qmax_w =
+      nvalid_w ? sd.pos_begin + (row0 + s * RW + nvalid_w - 1) * sd.pos_stride : kNoPos;
+  const int qmax_wg = sd.pos_begin + (row0 + rows_here - 1) * sd.pos_stride;
+
+  const int n_kv = sd.kv_len;
+  const int ntiles_all = (n_kv + BN - 1) / BN;
+  const int32_t *kvp = p.kv_pos ? p.kv_pos + sd.kv_begin : nullptr;
+  int n_wg, n_vis, n_full;
+  if (!p.causal) {
+    n_wg = n_vis = ntiles_all;
+    n_full = n_kv / BN;
+  } else if (!kvp) {
+    n_wg = (min(n_kv, max(qmax_wg + 1, 0)) + BN - 1) / BN;
+    n_vis = (min(n_kv, max(qmax_w + 1, 0)) + BN - 1) / BN;
+    n_full = min(n_kv, max(qmin_w + 1, 0)) / BN;
+  } else {
+    n_wg = n_vis = n_full = 0;
+    for (int t0 = 0; t0 < ntiles_all; t0 += 64) {
+      const int t = t0 + lane;
+      int first = INT_MAX, last = INT_MAX;
+      if (t < ntiles_all) {
+        first = kvp[t * BN];
+        if ((t + 1) * BN <= n_kv) last = kvp[t * BN + BN - 1];
+      }
+      n_wg += __builtin_popcountll(__builtin_amdgcn_ballot_w64(first <= qmax_wg));
+      n_vis += __builtin_popcountll(__builtin_amdgcn_ballot_w64(first <= qmax_w));
+      n_full += __builtin_popcountll(__builtin_amdgcn_ballot_w64(last <= qmin_w));
+    }
+  }
+  if (nvalid_w == 0) n_vis = n_full = 0;
+
+  // ---- LDS DMA: the score waves copy K (and wave 0 the key positions), the
+  // output waves V; same stage layout as attn_fwd_bf16_kernel
+  const __bf16 *kbase = (const __bf16 *)p.k + (int64_t)sd.kv_begin * p.k_rs + (int64_t)kvh * p.k_hs;
+  const __bf16 *vbase = (const __bf16 *)p.v + (int64_t)sd.kv_begin * p.v_rs + (int64_t)kvh * p.v_hs;
+  const uint32_t k_rb = (uint32_t)p.k_rs * 2u, v_rb = (uint32_t)p.v_rs * 2u;
+  const uint32_t k_lane = (uint32_t)(lane & 15) * k_rb + (uint32_t)(lane >> 4) * 16u;
+  const uint32_t v_lane =
+      (uint32_t)(4 * ((lane >> 2) / VCH) + (lane & 3)) * v_rb + (uint32_t)((lane >> 2) % VCH) * 16u;
+  auto issue = [&](int t) {
+    const int j0 = t * BN;
+    const int nrows = min(BN, n_kv - j0);
+    u32x4 *dst = sm[t % NBUF];
+    if (score) {
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(kbase + (int64_t)j0 * p.k_rs), (short)0, (int)(nrows * k_rb), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < C::KDMA; ++i) {
+        const int I = s * C::KDMA + i;
+        const uint32_t off = k_lane + (uint32_t)(16 * (4 * I / KCH)) * k_rb + (uint32_t)((4 * I) % KCH) * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void *)(dst + I * 64), 16, off, 0, 0, 0);
+      }
+      if (kvp && s == 0 && lane < BN) {
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kvp + j0), (short)0, nrows * 4, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            pr, (__attribute__((address_space(3))) void *)(dst + C::KPOS), 4, lane_id_here() * 4u,
+            0, 0, 0);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(vbase + (int64_t)j0 * p.v_rs), (short)0, (int)(nrows * v_rb), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < C::VDMA; ++i) {
+        const int I = s * C::VDMA + i;
+        const uint32_t off = v_lane + (uint32_t)(4 * (16 * I / VCH)) * v_rb;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void *)(dst + C::KUNITS + I * 64), 16, off, 0,
+            0, 0);
+      }
+    }
+  };
+  // iteration i begins: this wave's part of tile i has landed and its LDS
+  // operations of iteration i - 1 are done; after the barrier every wave has
+  // all of tile i and P(i - 2) of every score wave
+  auto top = [&](int i) {
+    const int later = min(n_wg - 1 - i, PREF - 1);
+    if (score) {
+      if (kvp && s == 0) wait_later_lgkm0<C::KDMA + 1, PREF - 1>(later);
+      else wait_later_lgkm0<C::KDMA, PREF - 1>(later);
+    } else {
+      wait_later_lgkm0<C::VDMA, PREF - 1>(later);
+    }
+    __builtin_amdgcn_s_barrier();
+    if (i + PREF < n_wg) issue(i + PREF);
+  };
+  auto stage = [&](int t) { return (const char *)sm[t % NBUF]; };
+
+#pragma unroll
+  for (int i = 0; i < PREF; ++i)
+    if (i < n_wg) issue(i);
+
+  const int li = lane & 15, bb = lane >> 4;
+  const int kq = ((n >> 4) * KCH + hf) * 256 + (n & 15) * 16;
+  const int vt = C::KUNITS * 16 +
+                 ((hf * VCH + 2 * (bb & 1) + ((li & 3) >> 1)) * 4 + (li >> 2)) * 16 + 8 * (li & 1);
+  const float sl2 = p.scale_log2;
+  bool bad = false;
+
+  if (score) {
+    // ---------------- score waves
+    // Their in-order instruction stream is the critical path of a tile: when
+    // both waves of a SIMD have a product ready, the score wave's goes first
+    // and the output wave's fill the matrix core while the score wave runs its
+    // exponentials (measured: 5 % faster than equal priorities).
+    __builtin_amdgcn_s_setprio(3);
+    bf16x8 qf[RB][KS];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int64_t qrow = (int64_t)sd.q_begin + row0 + s * RW + rb * 32 + n;
+      const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)h * p.q_hs + 8 * hf;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (valid[rb] && n_vis > 0) x = *(const u32x4 *)(qp + 16 * st);
+        qf[rb][st] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+    float m_ref[RB], l_run[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m_ref[rb] = -INFINITY;
+      l_run[rb] = 0.f;
+    }
+    auto qk = [&](f32x16 (&sc)[RB], const char *tl) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[rb][i] = 0.f;
+      constexpr int KLA = KS < 4 ? KS : 4;
+      bf16x8 kf[KLA];
+#pragma unroll
+      for (int st = 0; st < KLA; ++st) kf[st] = *(const bf16x8 *)(tl + kq + 512 * st);
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const bf16x8 a = kf[st % KLA];
+        if (st + KLA < KS) kf[st % KLA] = *(const bf16x8 *)(tl + kq + 512 * (st + KLA));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][st], sc[rb], 0, 0, 0);
+      }
+    };
+    auto mask = [&](f32x16 (&sc)[RB], const char *tl, int j0) {
+      const int *kp = (const int *)(tl + C::KPOS * 16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = 8 * (i >> 2) + 4 * hf + (i & 3);
+        const int kpos = kvp ? kp[kj] : j0 + kj;
+        const bool in = j0 + kj < n_kv;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const bool vis = in && (!p.causal || kpos <= qpos[rb]);
+          sc[rb][i] = vis ? sc[rb][i] : -INFINITY;
+        }
+      }
+    };
+    // exponentials of tile u (scores in sc) -> P(u) in the buffer u & 1, row sums
+    auto probs_out = [&](const f32x16 (&sc)[RB], int u) {
+      u32x4 *pw = &pbuf[u & 1][s][0][lane];
+      float ls[RB] = {};
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float mneg = (m_ref[rb] == -INFINITY) ? 0.f : -m_ref[rb];
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * c + 2 * e], sl2, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * c + 2 * e + 1], sl2, mneg));
+            ls[rb] += p0 + p1;
+            pk[e] = pack_bf16(p0, p1);
+          }
+          pw[(rb * 2 + c) * 64] = pk;
+        }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) l_run[rb] += ls[rb];
+    };
+    // before the exponentials of tile u: mask a boundary tile; the first tile
+    // fixes each row's reference
+    auto pre = [&](f32x16 (&sc)[RB], int u) {
+      if (u >= n_full) mask(sc, stage(u), u * BN);
+      if (u == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[rb][i]);
+          m_ref[rb] = max_xor32(m * sl2);
+        }
+      }
+    };
+    // iteration i of the steady state: S(i) -> nxt while P(i - 1) leaves cur
+    auto fused = [&](f32x16 (&cur)[RB], f32x16 (&nxt)[RB], int i) {
+      __builtin_amdgcn_iglp_opt(0);
+      qk(nxt, stage(i));
+      probs_out(cur, i - 1);
+    };
+    f32x16 sa[RB], sb[RB];
+    int i = 0;
+    top(0);
+    if (n_vis > 0) qk(sa, stage(0));
+    i = 1;
+    while (i + 1 < n_vis) {
+      top(i);
+      pre(sa, i - 1);
+      fused(sa, sb, i);
+      top(i + 1);
+      pre(sb, i);
+      fused(sb, sa, i + 1);
+      i += 2;
+    }
+    if (i < n_vis) {
+      top(i);
+      pre(sa, i - 1);
+      fused(sa, sb, i);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sa[rb] = sb[rb];
+      ++i;
+    }
+    if (n_vis > 0) {  // i == n_vis: the last visible tile's exponentials
+      top(i);
+      pre(sa, i - 1);
+      probs_out(sa, i - 1);
+      ++i;
+    }
+    for (; i < n_wg + 2; ++i) top(i);
+    // row sums and references for the output waves; a row sum above
+    // 2^kGrowMax (or not finite) flags the workgroup
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l_tot = sum_xor32(l_run[rb]);
+      bad = bad || !(l_tot <= kMaxSum);
+      if (hf == 0) {
+        s_l[s * RW + rb * 32 + n] = l_tot;
+        s_m[s * RW + rb * 32 + n] = m_ref[rb];
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) s_flag = 1;
+    __syncthreads();
+    if (tid == 0) flags[blockIdx.x] = s_flag;
+    return;  // the output waves write the rows
+  }
+
+  // ---------------- output waves
+  // iteration i multiplies P(i - 2) by V(i - 2), both complete at its barrier
+  f32x16 oacc[OB][RB];
+#pragma unroll
+  for (int b = 0; b < OB; ++b)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[b][rb][i] = 0.f;
+  // (the address of each transposing read is formed in a register: with the
+  // instruction's offset field instead, the kernel measured 30 % slower)
+  auto pv_read = [&](const char *tl, int c, u32x2 (&vl)[OB], u32x2 (&vh)[OB]) {
+#pragma unroll
+    for (int b = 0; b < OB; ++b) {
+      const char *vp = tl + vt + 64 * (4 * VCH * c + 4 * b);
+      vl[b] = lds_read_tr16(vp);
+      vh[b] = lds_read_tr16(vp + 64 * 2 * VCH);
+    }
+  };
+  auto pv_mma = [&](u32x2 (&vl)[OB], u32x2 (&vh)[OB], const bf16x8 (&pf)[RB]) {
+#pragma unroll
+    for (int b = 0; b < OB; ++b) {
+      const u32x4 av = {vl[b][0], vl[b][1], vh[b][0], vh[b][1]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        oacc[b][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb], oacc[b][rb], 0, 0, 0);
+    }
+  };
+  for (int i = 0; i < n_wg + 2; ++i) {
+    top(i);
+    const int u = i - 2;
+    if (u >= 0 && u < n_vis) {
+      const u32x4 *pr = &pbuf[u & 1][s][0][lane];
+      bf16x8 pf0[RB], pf1[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        pf0[rb] = __builtin_bit_cast(bf16x8, pr[(rb * 2 + 0) * 64]);
+        pf1[rb] = __builtin_bit_cast(bf16x8, pr[(rb * 2 + 1) * 64]);
+      }
+      const char *tl = stage(u);
+      u32x2 vl0[OB], vh0[OB], vl1[OB], vh1[OB];
+      pv_read(tl, 0, vl0, vh0);
+      pv_read(tl, 1, vl1, vh1);
+      lds_wait_later<2 * OB>(vl0, vh0);
+      pv_mma(vl0, vh0, pf0);
+      lds_wait_later<0>(vl1, vh1);
+      pv_mma(vl1, vh1, pf1);
+    }
+  }
+  // probabilities within range can still carry huge values of V past the
+  // fp32 range: a non-finite accumulator flags the workgroup too
+  {
+    bool fin = true;
+#pragma unroll
+    for (int b = 0; b < OB; ++b)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) fin = fin && __builtin_isfinite(oacc[b][rb][i]);
+    bad = !fin;
+  }
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) s_flag = 1;
+  __syncthreads();  // every wave is done with the tiles; flags and row sums are in
+  if (s_flag) return;  // the exact pass writes (or merges) these rows
+  float inv[RB], lse[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = s_l[s * RW + rb * 32 + n];
+    const float mr = s_m[s * RW + rb * 32 + n];
+    const bool any = l_tot > 0.f;
+    inv[rb] = any ? 1.f / l_tot : 0.f;
+    lse[rb] = any ? (mr + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+  // O^T -> LDS (wave-private staging) -> whole output rows
+  constexpr int OSZ = 4;
+  constexpr int OPITCH = DV * OSZ + 16;
+  static_assert(4 * 32 * OPITCH <= NBUF * C::STAGE * 16, "staging fits the stages");
+  char *ost = (char *)sm + s * 32 * OPITCH;
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int b = 0; b < OB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 x = make_float4(oacc[b][rb][4 * g] * inv[rb], oacc[b][rb][4 * g + 1] * inv[rb],
+                               oacc[b][rb][4 * g + 2] * inv[rb], oacc[b][rb][4 * g + 3] * inv[rb]);
+        *(float4 *)(ost + n * OPITCH + (32 * b + 8 * g + 4 * hf) * OSZ) = x;
+      }
+    if (hf == 0) s_lse[s * 32 + n] = lse[rb];
+    if (!p.accumulate && hf == 0 && valid[rb]) {
+      const int64_t orow = (int64_t)sd.o_begin + row0 + s * RW + rb * 32 + n;
+      p.lse[orow * p.lse_rs + h] = lse[rb];
+    }
+    constexpr int LPR = DV / 8;
+    constexpr int RPI = 64 / LPR;
+    const int sub = lane % LPR, rsub = lane / LPR;
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int r = r0 + rsub;
+      const int rr = s * RW + rb * 32 + r;
+      if (rr < rows_here) {
+        float4 a = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ);
+        float4 c = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ + 16);
+        const int64_t orow = (int64_t)sd.o_begin + row0 + rr;
+        if (p.accumulate && !merge_into(p, orow, h, sub * 8, s_lse[s * 32 + r], sub == 0, a, c))
+          continue;
+        if (p.o_bf16) {
+          u32x4 v;
+          v[0] = pack_bf16(a.x, a.y);
+          v[1] = pack_bf16(a.z, a.w);
+          v[2] = pack_bf16(c.x, c.y);
+          v[3] = pack_bf16(c.z, c.w);
+          *(u32x4 *)((__bf16 *)p.o + orow * p.o_rs + (int64_t)h * p.o_hs + sub * 8) = v;
+        } else {
+          float *op = (float *)p.o + orow * p.o_rs + (int64_t)h * p.o_hs + sub * 8;
+          *(float4 *)op = a;
+          *(float4 *)(op + 4) = c;
+        }
+      }
+    }
+  }
+}
+
 // main pass, then the exact pass over the workgroups it flagged
 template <int DQK, int DV, int RB>
 hipError_t launch_rb(const AttnParams &p, const LaunchSegs &L, hipStream_t stream) {
   const dim3 grid((unsigned)(L.num_tiles * p.hq));
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, RB, false>), grid, dim3(NT), 0, stream, p, L);
+  // the split-role main pass for qk 192 (measured 5-7 % faster there); for
+  // qk 128 it measured 9 % slower than the one-wave kernel, which keeps Q and
+  // O of 64 rows in its 512 registers
+  if constexpr (RB == 2 && DQK == 192)
+    hipLaunchKernelGGL((attn_fwd_bf16_split_kernel<DQK, DV>), grid, dim3(512), 0, stream, p, L);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, RB, false>), grid, dim3(NT), 0, stream, p, L);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, RB, true>), grid, dim3(NT), 0, stream, p, L);
