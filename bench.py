@@ -201,12 +201,12 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_kernel<192,128>",
+            "kernel": "attn_fwd_bf16_split_kernel<192,128> + exact pass attn_fwd_bf16_kernel<192,128,2,true>",
             "achieved": round(achieved_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": _profiled_traffic("attn_fwd_bf16_kernel<192,128>", "attn_fwd_bf16.hip"),
+            "traffic": _profiled_traffic("attn_fwd_bf16_split_kernel<192,128>", "attn_fwd_bf16.hip"),
             "algorithmic_bytes": attn_bytes,
             "avg_launch_ms": round(attn_launch_ms, 4),
         },
@@ -441,7 +441,7 @@ def _decode(cp, w):
     return {"shard_ms": round(ms, 4), "algorithmic_bytes_per_shard": by,
             "GB/s": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
             "TFLOP/s": round(fl / ms / 1e9, 1), "workspace_bytes": int(ws.numel()),
-            "traffic": _profiled_traffic("attn_decode_mla_kernel", "attn_decode_mla.hip"),
+            "traffic": _profiled_traffic("attn_decode_px_kernel", "attn_decode_mla.hip"),
             "merge_ms": round(mms, 4), "merge_GB/s": round(mby / mms / 1e6, 1),
             "merge_frac_hbm": round(mby / mms / 1e6 / PEAK_HBM_GBS, 4),
             "merge_cache_resident_ms": round(mms_warm, 4),
@@ -501,7 +501,7 @@ def _decode_paged(cp, w, bs):
             "paged_GB/s": round(by / paged / 1e6, 1),
             "paged_frac_hbm": round(by / paged / 1e6 / PEAK_HBM_GBS, 4),
             "paged_over_contiguous": round(paged / cont, 4),
-            "traffic_contiguous": _profiled_traffic("attn_decode_mla_kernel", "attn_decode_mla.hip")}
+            "traffic_contiguous": _profiled_traffic("attn_decode_px_kernel", "attn_decode_mla.hip")}
 
 
 def _cpu_baseline(w, q, k, v, plan, budget_s):
