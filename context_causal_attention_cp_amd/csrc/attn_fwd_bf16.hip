@@ -725,6 +725,60 @@ __device__ inline uint32_t lane_id_here() {
   return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z));
 }
 
+// LDS accesses of the split-role main pass, all through inline asm.  The
+// compiler's wait-count pass cannot tell an LDS access from the LDS-DMA
+// writes still in flight into other stages; for a compiler-visible LDS read
+// or write in the loop it may drain every outstanding DMA (vmcnt(0)) first,
+// which empties the prefetch pipeline (measured: 30 % slower whenever it
+// appears).  These accesses are invisible to that pass; their completion is
+// waited for explicitly (lgkmcnt) with the result registers tied to the wait.
+template <int OFF>
+__device__ inline u32x4 lds_read_b128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ inline void lds_write_b128_at(uint32_t addr, u32x4 v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+// complete once at most LATER LDS operations issued after it are pending
+template <int LATER, typename T>
+__device__ inline void lds_wait_tie(T &x) {
+  static_assert(LATER >= 0 && LATER < 16, "lgkmcnt");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(LATER));
+}
+__device__ inline uint32_t lds_u32(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+// S^T = K Q^T of one tile, k-step ST onwards: the fragment of step ST was read
+// KLA steps earlier; the read of step ST + KLA goes out once it is consumed
+template <int ST, int KS, int KLA, int RB>
+__device__ inline void split_qk(uint32_t ka, bf16x8 (&kf)[KLA], const bf16x8 (&qf)[RB][KS],
+                                f32x16 (&sc)[RB]) {
+  if constexpr (ST < KS) {
+    constexpr int LATER = (KS - 1 - ST) < (KLA - 1) ? (KS - 1 - ST) : (KLA - 1);
+    lds_wait_tie<LATER>(kf[ST % KLA]);
+    const bf16x8 a = kf[ST % KLA];
+    if constexpr (ST + KLA < KS)
+      kf[ST % KLA] = __builtin_bit_cast(bf16x8, lds_read_b128_at<512 * (ST + KLA)>(ka));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][ST], sc[rb], 0, 0, 0);
+    split_qk<ST + 1, KS, KLA, RB>(ka, kf, qf, sc);
+  }
+}
+template <int ST, int KLA>
+__device__ inline void split_k_first(uint32_t ka, bf16x8 (&kf)[KLA]) {
+  if constexpr (ST < KLA) {
+    kf[ST] = __builtin_bit_cast(bf16x8, lds_read_b128_at<512 * ST>(ka));
+    split_k_first<ST + 1, KLA>(ka, kf);
+  }
+}
+
 // Stages of the split-role main pass: the probabilities of a tile take a
 // double buffer of 2 x 4 waves x 4 KiB next to the K/V stages.
 template <int DQK, int DV>
@@ -922,64 +976,85 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
       m_ref[rb] = -INFINITY;
       l_run[rb] = 0.f;
     }
-    auto qk = [&](f32x16 (&sc)[RB], const char *tl) {
+    const uint32_t kq_lds = lds_u32(sm) + (uint32_t)kq;
+    auto qk = [&](f32x16 (&sc)[RB], int t) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[rb][i] = 0.f;
       constexpr int KLA = KS < 4 ? KS : 4;
+      const uint32_t ka = kq_lds + (uint32_t)((t % NBUF) * C::STAGE * 16);
       bf16x8 kf[KLA];
-#pragma unroll
-      for (int st = 0; st < KLA; ++st) kf[st] = *(const bf16x8 *)(tl + kq + 512 * st);
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const bf16x8 a = kf[st % KLA];
-        if (st + KLA < KS) kf[st % KLA] = *(const bf16x8 *)(tl + kq + 512 * (st + KLA));
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][st], sc[rb], 0, 0, 0);
-      }
+      split_k_first<0, KLA>(ka, kf);
+      split_qk<0, KS, KLA, RB>(ka, kf, qf, sc);
     };
-    auto mask = [&](f32x16 (&sc)[RB], const char *tl, int j0) {
-      const int *kp = (const int *)(tl + C::KPOS * 16);
+    auto mask = [&](f32x16 (&sc)[RB], int u) {
+      const int j0 = u * BN;
+      const int hm = (int)(lane_id_here() >> 5);  // (read again: see the epilogue below)
+      int kpos[16];
+      if (kvp) {
+        // this lane's keys: 4 runs of 4 consecutive positions (8g + 4hm + 0..3)
+        const uint32_t pa = lds_u32(sm[u % NBUF]) + (uint32_t)(C::KPOS * 16 + 16 * hm);
+        u32x4 r0 = lds_read_b128_at<0>(pa), r1 = lds_read_b128_at<32>(pa);
+        u32x4 r2 = lds_read_b128_at<64>(pa), r3 = lds_read_b128_at<96>(pa);
+        lds_wait_tie<3>(r0);
+        lds_wait_tie<2>(r1);
+        lds_wait_tie<1>(r2);
+        lds_wait_tie<0>(r3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kpos[e] = (int)r0[e];
+          kpos[4 + e] = (int)r1[e];
+          kpos[8 + e] = (int)r2[e];
+          kpos[12 + e] = (int)r3[e];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kpos[i] = j0 + 8 * (i >> 2) + 4 * hm + (i & 3);
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kj = 8 * (i >> 2) + 4 * hf + (i & 3);
-        const int kpos = kvp ? kp[kj] : j0 + kj;
+        const int kj = 8 * (i >> 2) + 4 * hm + (i & 3);
         const bool in = j0 + kj < n_kv;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const bool vis = in && (!p.causal || kpos <= qpos[rb]);
+          const bool vis = in && (!p.causal || kpos[i] <= qpos[rb]);
           sc[rb][i] = vis ? sc[rb][i] : -INFINITY;
         }
       }
     };
     // exponentials of tile u (scores in sc) -> P(u) in the buffer u & 1, row sums
+    const uint32_t pw_lds = lds_u32(&pbuf[0][s][0][lane]);
     auto probs_out = [&](const f32x16 (&sc)[RB], int u) {
-      u32x4 *pw = &pbuf[u & 1][s][0][lane];
+      const uint32_t pw = pw_lds + (uint32_t)((u & 1) * 4 * 2 * RB * 64 * 16);
       float ls[RB] = {};
+      u32x4 pk[2][RB];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const float mneg = (m_ref[rb] == -INFINITY) ? 0.f : -m_ref[rb];
-          u32x4 pk;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * c + 2 * e], sl2, mneg));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * c + 2 * e + 1], sl2, mneg));
             ls[rb] += p0 + p1;
-            pk[e] = pack_bf16(p0, p1);
+            pk[c][rb][e] = pack_bf16(p0, p1);
           }
-          pw[(rb * 2 + c) * 64] = pk;
         }
+      // P(u) as [rb * 2 + c][lane] units of the wave's buffer
+      static_assert(RB == 2, "P layout");
+      lds_write_b128_at<0 * 1024>(pw, pk[0][0]);
+      lds_write_b128_at<1 * 1024>(pw, pk[1][0]);
+      lds_write_b128_at<2 * 1024>(pw, pk[0][1]);
+      lds_write_b128_at<3 * 1024>(pw, pk[1][1]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) l_run[rb] += ls[rb];
     };
     // before the exponentials of tile u: mask a boundary tile; the first tile
     // fixes each row's reference
     auto pre = [&](f32x16 (&sc)[RB], int u) {
-      if (u >= n_full) mask(sc, stage(u), u * BN);
+      if (u >= n_full) mask(sc, u);
       if (u == 0) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -993,13 +1068,13 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
     // iteration i of the steady state: S(i) -> nxt while P(i - 1) leaves cur
     auto fused = [&](f32x16 (&cur)[RB], f32x16 (&nxt)[RB], int i) {
       __builtin_amdgcn_iglp_opt(0);
-      qk(nxt, stage(i));
+      qk(nxt, i);
       probs_out(cur, i - 1);
     };
     f32x16 sa[RB], sb[RB];
     int i = 0;
     top(0);
-    if (n_vis > 0) qk(sa, stage(0));
+    if (n_vis > 0) qk(sa, 0);
     i = 1;
     while (i + 1 < n_vis) {
       top(i);
@@ -1027,16 +1102,19 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
     for (; i < n_wg + 2; ++i) top(i);
     // row sums and references for the output waves; a row sum above
     // 2^kGrowMax (or not finite) flags the workgroup
+    // (the lane index is read again here rather than kept across the loop,
+    // where it would take a register the loop needs)
+    const int ln = (int)lane_id_here();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float l_tot = sum_xor32(l_run[rb]);
       bad = bad || !(l_tot <= kMaxSum);
-      if (hf == 0) {
-        s_l[s * RW + rb * 32 + n] = l_tot;
-        s_m[s * RW + rb * 32 + n] = m_ref[rb];
+      if (ln < 32) {
+        s_l[s * RW + rb * 32 + ln] = l_tot;
+        s_m[s * RW + rb * 32 + ln] = m_ref[rb];
       }
     }
-    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) s_flag = 1;
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && ln == 0) s_flag = 1;
     __syncthreads();
     if (tid == 0) flags[blockIdx.x] = s_flag;
     return;  // the output waves write the rows
@@ -1051,8 +1129,6 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[b][rb][i] = 0.f;
-  // (the address of each transposing read is formed in a register: with the
-  // instruction's offset field instead, the kernel measured 30 % slower)
   auto pv_read = [&](const char *tl, int c, u32x2 (&vl)[OB], u32x2 (&vh)[OB]) {
 #pragma unroll
     for (int b = 0; b < OB; ++b) {
@@ -1071,24 +1147,30 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
         oacc[b][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb], oacc[b][rb], 0, 0, 0);
     }
   };
+  const uint32_t pr_lds = lds_u32(&pbuf[0][s][0][lane]);
   for (int i = 0; i < n_wg + 2; ++i) {
     top(i);
     const int u = i - 2;
     if (u >= 0 && u < n_vis) {
-      const u32x4 *pr = &pbuf[u & 1][s][0][lane];
-      bf16x8 pf0[RB], pf1[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        pf0[rb] = __builtin_bit_cast(bf16x8, pr[(rb * 2 + 0) * 64]);
-        pf1[rb] = __builtin_bit_cast(bf16x8, pr[(rb * 2 + 1) * 64]);
-      }
+      const uint32_t pr = pr_lds + (uint32_t)((u & 1) * 4 * 2 * RB * 64 * 16);
+      static_assert(RB == 2, "P layout");
+      u32x4 q00 = lds_read_b128_at<0 * 1024>(pr), q01 = lds_read_b128_at<1 * 1024>(pr);
+      u32x4 q10 = lds_read_b128_at<2 * 1024>(pr), q11 = lds_read_b128_at<3 * 1024>(pr);
       const char *tl = stage(u);
       u32x2 vl0[OB], vh0[OB], vl1[OB], vh1[OB];
       pv_read(tl, 0, vl0, vh0);
       pv_read(tl, 1, vl1, vh1);
+      // the P reads and the first key step's V^T reads are done once at most
+      // the second step's 2 * OB reads are pending
       lds_wait_later<2 * OB>(vl0, vh0);
+      lds_wait_tie<2 * OB>(q00);
+      lds_wait_tie<2 * OB>(q10);
+      const bf16x8 pf0[RB] = {__builtin_bit_cast(bf16x8, q00), __builtin_bit_cast(bf16x8, q10)};
       pv_mma(vl0, vh0, pf0);
       lds_wait_later<0>(vl1, vh1);
+      lds_wait_tie<0>(q01);
+      lds_wait_tie<0>(q11);
+      const bf16x8 pf1[RB] = {__builtin_bit_cast(bf16x8, q01), __builtin_bit_cast(bf16x8, q11)};
       pv_mma(vl1, vh1, pf1);
     }
   }
