@@ -803,7 +803,8 @@ struct SplitCfg {
 //                 S(i - 1), which go to LDS as P(i - 1) (bf16, already in the
 //                 B-operand layout of the PV product: lane l of the output
 //                 wave reads what lane l of its score wave wrote);
-//   output waves: O^T += V(i - 2)^T P(i - 2)^T.
+//   output waves: O^T += V(i - 3)^T P(i - 3)^T from registers, then the reads
+//                 of V(i - 2) and P(i - 2) for the next iteration.
 // The arithmetic and its order are those of attn_fwd_bf16_kernel<.., 2, false>
 // (same scores, same bf16 probabilities, same row sums, same product order),
 // so outputs, log-sum-exps and flags are bitwise the same; the exact pass of
@@ -1121,7 +1122,6 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   }
 
   // ---------------- output waves
-  // iteration i multiplies P(i - 2) by V(i - 2), both complete at its barrier
   f32x16 oacc[OB][RB];
 #pragma unroll
   for (int b = 0; b < OB; ++b)
@@ -1147,32 +1147,47 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
         oacc[b][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb], oacc[b][rb], 0, 0, 0);
     }
   };
+  // Iteration i multiplies P(i - 3) and V(i - 3), read into registers at the
+  // end of iteration i - 1 (both were complete at its barrier), so the
+  // products start right after the barrier instead of behind the burst of
+  // LDS reads every wave issues there; then it reads P(i - 2) and V(i - 2)
+  // for the next iteration (complete at the next barrier: top() waits for
+  // this wave's LDS operations).
   const uint32_t pr_lds = lds_u32(&pbuf[0][s][0][lane]);
+  static_assert(RB == 2, "P layout");
+  u32x4 q00, q01, q10, q11;
+  u32x2 vl0[OB], vh0[OB], vl1[OB], vh1[OB];
+  auto pv_reads = [&](int u) {
+    const uint32_t pr = pr_lds + (uint32_t)((u & 1) * 4 * 2 * RB * 64 * 16);
+    q00 = lds_read_b128_at<0 * 1024>(pr);
+    q01 = lds_read_b128_at<1 * 1024>(pr);
+    q10 = lds_read_b128_at<2 * 1024>(pr);
+    q11 = lds_read_b128_at<3 * 1024>(pr);
+    const char *tl = stage(u);
+    pv_read(tl, 0, vl0, vh0);
+    pv_read(tl, 1, vl1, vh1);
+  };
+  auto pv_products = [&]() {
+    // (complete since the barrier; the waits order the products after it)
+    lds_wait_later<0>(vl0, vh0);
+    lds_wait_later<0>(vl1, vh1);
+    lds_wait_tie<0>(q00);
+    lds_wait_tie<0>(q01);
+    lds_wait_tie<0>(q10);
+    lds_wait_tie<0>(q11);
+    const bf16x8 pf0[RB] = {__builtin_bit_cast(bf16x8, q00), __builtin_bit_cast(bf16x8, q10)};
+    const bf16x8 pf1[RB] = {__builtin_bit_cast(bf16x8, q01), __builtin_bit_cast(bf16x8, q11)};
+    pv_mma(vl0, vh0, pf0);
+    pv_mma(vl1, vh1, pf1);
+  };
   for (int i = 0; i < n_wg + 2; ++i) {
     top(i);
-    const int u = i - 2;
-    if (u >= 0 && u < n_vis) {
-      const uint32_t pr = pr_lds + (uint32_t)((u & 1) * 4 * 2 * RB * 64 * 16);
-      static_assert(RB == 2, "P layout");
-      u32x4 q00 = lds_read_b128_at<0 * 1024>(pr), q01 = lds_read_b128_at<1 * 1024>(pr);
-      u32x4 q10 = lds_read_b128_at<2 * 1024>(pr), q11 = lds_read_b128_at<3 * 1024>(pr);
-      const char *tl = stage(u);
-      u32x2 vl0[OB], vh0[OB], vl1[OB], vh1[OB];
-      pv_read(tl, 0, vl0, vh0);
-      pv_read(tl, 1, vl1, vh1);
-      // the P reads and the first key step's V^T reads are done once at most
-      // the second step's 2 * OB reads are pending
-      lds_wait_later<2 * OB>(vl0, vh0);
-      lds_wait_tie<2 * OB>(q00);
-      lds_wait_tie<2 * OB>(q10);
-      const bf16x8 pf0[RB] = {__builtin_bit_cast(bf16x8, q00), __builtin_bit_cast(bf16x8, q10)};
-      pv_mma(vl0, vh0, pf0);
-      lds_wait_later<0>(vl1, vh1);
-      lds_wait_tie<0>(q01);
-      lds_wait_tie<0>(q11);
-      const bf16x8 pf1[RB] = {__builtin_bit_cast(bf16x8, q01), __builtin_bit_cast(bf16x8, q11)};
-      pv_mma(vl1, vh1, pf1);
-    }
+    if (i >= 3 && i - 3 < n_vis) pv_products();
+    if (i >= 2 && i - 2 < n_vis) pv_reads(i - 2);
+  }
+  if (n_wg >= 1 && n_wg - 1 < n_vis) {  // the last tile, read in the last iteration
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    pv_products();
   }
   // probabilities within range can still carry huge values of V past the
   // fp32 range: a non-finite accumulator flags the workgroup too
