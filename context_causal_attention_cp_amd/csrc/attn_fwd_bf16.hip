@@ -49,6 +49,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <utility>
 
 #include "internal.h"
 
@@ -733,6 +734,22 @@ __device__ inline uint32_t lane_id_here() {
 // appears).  These accesses are invisible to that pass; their completion is
 // waited for explicitly (lgkmcnt) with the result registers tied to the wait.
 template <int OFF>
+__device__ inline u32x2 lds_read_tr16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// the V^T fragments of 16-key step C of a stage (addr: the stage's LDS address
+// plus this lane's offset), one pair of reads per 32-row dv block B
+template <int VCH, int OB, int C, int... B>
+__device__ inline void split_tr_reads(uint32_t addr, u32x2 (&vl)[OB], u32x2 (&vh)[OB],
+                                      std::integer_sequence<int, B...>) {
+  ((vl[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B)>(addr),
+    vh[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B) + 128 * VCH>(addr)),
+   ...);
+}
+template <int OFF>
 __device__ inline u32x4 lds_read_b128_at(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset");
   u32x4 r;
@@ -1129,14 +1146,6 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[b][rb][i] = 0.f;
-  auto pv_read = [&](const char *tl, int c, u32x2 (&vl)[OB], u32x2 (&vh)[OB]) {
-#pragma unroll
-    for (int b = 0; b < OB; ++b) {
-      const char *vp = tl + vt + 64 * (4 * VCH * c + 4 * b);
-      vl[b] = lds_read_tr16(vp);
-      vh[b] = lds_read_tr16(vp + 64 * 2 * VCH);
-    }
-  };
   auto pv_mma = [&](u32x2 (&vl)[OB], u32x2 (&vh)[OB], const bf16x8 (&pf)[RB]) {
 #pragma unroll
     for (int b = 0; b < OB; ++b) {
@@ -1163,9 +1172,9 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
     q01 = lds_read_b128_at<1 * 1024>(pr);
     q10 = lds_read_b128_at<2 * 1024>(pr);
     q11 = lds_read_b128_at<3 * 1024>(pr);
-    const char *tl = stage(u);
-    pv_read(tl, 0, vl0, vh0);
-    pv_read(tl, 1, vl1, vh1);
+    const uint32_t va = lds_u32(stage(u)) + (uint32_t)vt;
+    split_tr_reads<VCH, OB, 0>(va, vl0, vh0, std::make_integer_sequence<int, OB>{});
+    split_tr_reads<VCH, OB, 1>(va, vl1, vh1, std::make_integer_sequence<int, OB>{});
   };
   auto pv_products = [&]() {
     // (complete since the barrier; the waits order the products after it)
