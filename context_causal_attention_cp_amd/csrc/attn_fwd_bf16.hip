@@ -37,8 +37,8 @@
 // ones streaming the same K/V share that XCD's L2; inside a head the
 // heaviest tiles (longest causal extent) start first.
 //
-// For qk 192 (the MLA shape) the main pass of 256-row workgroups runs as
-// attn_fwd_bf16_split_kernel instead: 8 waves, two per SIMD, the score waves
+// For qk 192 (the MLA shape) and qk 128 the main pass of 256-row workgroups runs
+// as attn_fwd_bf16_split_kernel instead: 8 waves, two per SIMD, the score waves
 // holding Q and the output waves holding O of the same 64 rows, with the
 // probabilities handed over through LDS.  A single wave per SIMD issues its
 // products, exponentials, DMA descriptors and waits in order and leaves the
@@ -1275,10 +1275,9 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
 template <int DQK, int DV, int RB>
 hipError_t launch_rb(const AttnParams &p, const LaunchSegs &L, hipStream_t stream) {
   const dim3 grid((unsigned)(L.num_tiles * p.hq));
-  // the split-role main pass for qk 192 (measured 5-7 % faster there); for
-  // qk 128 it measured 9 % slower than the one-wave kernel, which keeps Q and
-  // O of 64 rows in its 512 registers
-  if constexpr (RB == 2 && DQK == 192)
+  // the split-role main pass for 256-row workgroups at qk 192 and 128
+  // (measured 9-10 % faster than the one-wave kernel at both)
+  if constexpr (RB == 2 && (DQK == 192 || DQK == 128))
     hipLaunchKernelGGL((attn_fwd_bf16_split_kernel<DQK, DV>), grid, dim3(512), 0, stream, p, L);
   else
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<DQK, DV, RB, false>), grid, dim3(NT), 0, stream, p, L);
