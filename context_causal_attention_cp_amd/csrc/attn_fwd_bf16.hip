@@ -202,6 +202,85 @@ __device__ inline bool merge_into(const AttnParams &p, int64_t orow, int h, int 
   return true;
 }
 
+// This lane's index, recomputed where it is used (2 VALU): an asm barrier on
+// the input keeps the compiler from hoisting it out of the loop and holding
+// it (or spilling it) across the loop.
+__device__ inline uint32_t lane_id_here() {
+  uint32_t z = 0;
+  asm volatile("" : "+v"(z));
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z));
+}
+
+// LDS accesses inside the key loops, all through inline asm.  The
+// compiler's wait-count pass cannot tell an LDS access from the LDS-DMA
+// writes still in flight into other stages; for a compiler-visible LDS read
+// or write in the loop it may drain every outstanding DMA (vmcnt(0)) first,
+// which empties the prefetch pipeline (measured: 30 % slower whenever it
+// appears).  These accesses are invisible to that pass; their completion is
+// waited for explicitly (lgkmcnt) with the result registers tied to the wait.
+template <int OFF>
+__device__ inline u32x2 lds_read_tr16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// the V^T fragments of 16-key step C of a stage (addr: the stage's LDS address
+// plus this lane's offset), one pair of reads per 32-row dv block B
+template <int VCH, int OB, int C, int... B>
+__device__ inline void split_tr_reads(uint32_t addr, u32x2 (&vl)[OB], u32x2 (&vh)[OB],
+                                      std::integer_sequence<int, B...>) {
+  ((vl[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B)>(addr),
+    vh[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B) + 128 * VCH>(addr)),
+   ...);
+}
+template <int OFF>
+__device__ inline u32x4 lds_read_b128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ inline void lds_write_b128_at(uint32_t addr, u32x4 v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+// complete once at most LATER LDS operations issued after it are pending
+template <int LATER, typename T>
+__device__ inline void lds_wait_tie(T &x) {
+  static_assert(LATER >= 0 && LATER < 16, "lgkmcnt");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(LATER));
+}
+__device__ inline uint32_t lds_u32(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+// S^T = K Q^T of one tile, k-step ST onwards: the fragment of step ST was read
+// KLA steps earlier; the read of step ST + KLA goes out once it is consumed
+template <int ST, int KS, int KLA, int RB>
+__device__ inline void split_qk(uint32_t ka, bf16x8 (&kf)[KLA], const bf16x8 (&qf)[RB][KS],
+                                f32x16 (&sc)[RB]) {
+  if constexpr (ST < KS) {
+    constexpr int LATER = (KS - 1 - ST) < (KLA - 1) ? (KS - 1 - ST) : (KLA - 1);
+    lds_wait_tie<LATER>(kf[ST % KLA]);
+    const bf16x8 a = kf[ST % KLA];
+    if constexpr (ST + KLA < KS)
+      kf[ST % KLA] = __builtin_bit_cast(bf16x8, lds_read_b128_at<512 * (ST + KLA)>(ka));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][ST], sc[rb], 0, 0, 0);
+    split_qk<ST + 1, KS, KLA, RB>(ka, kf, qf, sc);
+  }
+}
+template <int ST, int KLA>
+__device__ inline void split_k_first(uint32_t ka, bf16x8 (&kf)[KLA]) {
+  if constexpr (ST < KLA) {
+    kf[ST] = __builtin_bit_cast(bf16x8, lds_read_b128_at<512 * ST>(ka));
+    split_k_first<ST + 1, KLA>(ka, kf);
+  }
+}
+
 // LDS layouts of one stage (16-byte units; keys fastest, so no swizzle):
 //   K  unit ((key/16)*KCH + chunk)*16 + key%16   -- a K fragment read (32 keys
 //      of one chunk) is 2 x 256 contiguous bytes;
@@ -417,38 +496,50 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   }
   const float sl2 = p.scale_log2;
 
-  // S^T = K Q^T of one tile (32 keys x RB row blocks)
+  // S^T = K Q^T of one tile (32 keys x RB row blocks); K fragments rotate
+  // through KLA registers, each read issued KLA k-steps before its use (hides
+  // the LDS latency behind the products)
   auto qk = [&](f32x16 (&sc)[RB], const char *tl) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[rb][i] = 0.f;
-    // K fragments rotate through KLA registers, each read issued KLA k-steps
-    // before its use (hides the LDS latency behind the products)
     constexpr int KLA = KS < 4 ? KS : 4;
+    const uint32_t ka = lds_u32(tl) + (uint32_t)kq;
     bf16x8 kf[KLA];
-#pragma unroll
-    for (int st = 0; st < KLA; ++st) kf[st] = *(const bf16x8 *)(tl + kq + 512 * st);
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const bf16x8 a = kf[st % KLA];
-      if (st + KLA < KS) kf[st % KLA] = *(const bf16x8 *)(tl + kq + 512 * (st + KLA));
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][st], sc[rb], 0, 0, 0);
-    }
+    split_k_first<0, KLA>(ka, kf);
+    split_qk<0, KS, KLA, RB>(ka, kf, qf, sc);
   };
   // boundary tiles: keys past the segment or after the row's position
   auto mask = [&](f32x16 (&sc)[RB], const char *tl, int j0) {
-    const int *kp = (const int *)(tl + C::KPOS * 16);
+    int kpos[16];
+    if (kvp) {
+      // this lane's keys: 4 runs of 4 consecutive positions (8g + 4hf + 0..3)
+      const uint32_t pa = lds_u32(tl) + (uint32_t)(C::KPOS * 16 + 16 * hf);
+      u32x4 r0 = lds_read_b128_at<0>(pa), r1 = lds_read_b128_at<32>(pa);
+      u32x4 r2 = lds_read_b128_at<64>(pa), r3 = lds_read_b128_at<96>(pa);
+      lds_wait_tie<3>(r0);
+      lds_wait_tie<2>(r1);
+      lds_wait_tie<1>(r2);
+      lds_wait_tie<0>(r3);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kpos[e] = (int)r0[e];
+        kpos[4 + e] = (int)r1[e];
+        kpos[8 + e] = (int)r2[e];
+        kpos[12 + e] = (int)r3[e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) kpos[i] = j0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kj = 8 * (i >> 2) + 4 * hf + (i & 3);
-      const int kpos = kvp ? kp[kj] : j0 + kj;
       const bool in = j0 + kj < n_kv;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const bool vis = in && (!p.causal || kpos <= qpos[rb]);
+        const bool vis = in && (!p.causal || kpos[i] <= qpos[rb]);
         sc[rb][i] = vis ? sc[rb][i] : -INFINITY;
       }
     }
@@ -715,85 +806,6 @@ __device__ inline void wait_later_lgkm0(int later) {
   if constexpr (MAXL >= 2) if (later == 2) { wait_vm_lgkm0<2 * PER>(); return; }
   if constexpr (MAXL >= 1) if (later == 1) { wait_vm_lgkm0<PER>(); return; }
   wait_vm_lgkm0<0>();
-}
-
-// This lane's index, recomputed where it is used (2 VALU): an asm barrier on
-// the input keeps the compiler from hoisting it out of the loop and holding
-// it (or spilling it) across the loop.
-__device__ inline uint32_t lane_id_here() {
-  uint32_t z = 0;
-  asm volatile("" : "+v"(z));
-  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z));
-}
-
-// LDS accesses of the split-role main pass, all through inline asm.  The
-// compiler's wait-count pass cannot tell an LDS access from the LDS-DMA
-// writes still in flight into other stages; for a compiler-visible LDS read
-// or write in the loop it may drain every outstanding DMA (vmcnt(0)) first,
-// which empties the prefetch pipeline (measured: 30 % slower whenever it
-// appears).  These accesses are invisible to that pass; their completion is
-// waited for explicitly (lgkmcnt) with the result registers tied to the wait.
-template <int OFF>
-__device__ inline u32x2 lds_read_tr16_at(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-// the V^T fragments of 16-key step C of a stage (addr: the stage's LDS address
-// plus this lane's offset), one pair of reads per 32-row dv block B
-template <int VCH, int OB, int C, int... B>
-__device__ inline void split_tr_reads(uint32_t addr, u32x2 (&vl)[OB], u32x2 (&vh)[OB],
-                                      std::integer_sequence<int, B...>) {
-  ((vl[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B)>(addr),
-    vh[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B) + 128 * VCH>(addr)),
-   ...);
-}
-template <int OFF>
-__device__ inline u32x4 lds_read_b128_at(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-template <int OFF>
-__device__ inline void lds_write_b128_at(uint32_t addr, u32x4 v) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
-  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
-}
-// complete once at most LATER LDS operations issued after it are pending
-template <int LATER, typename T>
-__device__ inline void lds_wait_tie(T &x) {
-  static_assert(LATER >= 0 && LATER < 16, "lgkmcnt");
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(LATER));
-}
-__device__ inline uint32_t lds_u32(const void *p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
-}
-
-// S^T = K Q^T of one tile, k-step ST onwards: the fragment of step ST was read
-// KLA steps earlier; the read of step ST + KLA goes out once it is consumed
-template <int ST, int KS, int KLA, int RB>
-__device__ inline void split_qk(uint32_t ka, bf16x8 (&kf)[KLA], const bf16x8 (&qf)[RB][KS],
-                                f32x16 (&sc)[RB]) {
-  if constexpr (ST < KS) {
-    constexpr int LATER = (KS - 1 - ST) < (KLA - 1) ? (KS - 1 - ST) : (KLA - 1);
-    lds_wait_tie<LATER>(kf[ST % KLA]);
-    const bf16x8 a = kf[ST % KLA];
-    if constexpr (ST + KLA < KS)
-      kf[ST % KLA] = __builtin_bit_cast(bf16x8, lds_read_b128_at<512 * (ST + KLA)>(ka));
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][ST], sc[rb], 0, 0, 0);
-    split_qk<ST + 1, KS, KLA, RB>(ka, kf, qf, sc);
-  }
-}
-template <int ST, int KLA>
-__device__ inline void split_k_first(uint32_t ka, bf16x8 (&kf)[KLA]) {
-  if constexpr (ST < KLA) {
-    kf[ST] = __builtin_bit_cast(bf16x8, lds_read_b128_at<512 * ST>(ka));
-    split_k_first<ST + 1, KLA>(ka, kf);
-  }
 }
 
 // Stages of the split-role main pass: the probabilities of a tile take a
