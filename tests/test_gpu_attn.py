@@ -174,26 +174,29 @@ def test_repeatable_bitwise():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-GROWTH = [(300, 4, 0.1, 1), (300, 4, 0.5, 1), (4096, 128, 0.5, 1), (300, 4, 0.36, 1),
-          (4096, 128, 0.23, 2)]
-GROWTH_IDS = ["small-2^27", "small-2^138", "large-2^138", "small-2^100", "large-2x2^63.6"]
+GROWTH = [(300, 4, 0.1, 1, 192), (300, 4, 0.5, 1, 192), (4096, 128, 0.5, 1, 192),
+          (300, 4, 0.36, 1, 192), (4096, 128, 0.23, 2, 192), (4096, 128, 0.146, 1, 128),
+          (4096, 128, 0.5415, 1, 128)]
+GROWTH_IDS = ["small-2^27", "small-2^138", "large-2^138", "small-2^100", "large-2x2^63.6",
+              "large-d128-2^27", "large-d128-2^100"]
 
 
 @pytest.mark.parametrize("accumulate", [False, True], ids=["write", "accumulate"])
-@pytest.mark.parametrize("rows,hq,val,nbig", GROWTH, ids=GROWTH_IDS)
-def test_reference_growth(rows, hq, val, nbig, accumulate):
+@pytest.mark.parametrize("rows,hq,val,nbig,dqk", GROWTH, ids=GROWTH_IDS)
+def test_reference_growth(rows, hq, val, nbig, dqk, accumulate):
     """Keys, in a late tile, far above every score of the first tile: with
-    q = 1 and keys 0 except keys 900.. = val (192 dims, scale 1) the row max
-    grows by 192*val*log2(e) in log2 units -- 2^27 (kept by the main pass),
+    q = 1 and keys 0 except keys 900.. = val (d dims, scale 1) the row max
+    grows by d*val*log2(e) in log2 units -- 2^27 (kept by the main pass),
     2^100 or 2^138 (probabilities above 2^64, or beyond fp32 range: the
     workgroup is flagged and recomputed), or twice 2^63.6 (no probability
     above 2^64 but a row sum above it: flagged as well).  128-row and
-    256-row workgroups; the plain definition decides.
+    256-row workgroups (4096 rows x 128 heads: the split-role main pass, at
+    qk 192 and 128); the plain definition decides.
     accumulate: keys 0..449 are first written by a plain call, then keys
     450..999 (with the large ones) are merged into that running (O, LSE) by
     an accumulating call; a flagged workgroup must merge exactly once (in
     the exact pass), which the dense result over all keys checks."""
-    n_kv, dqk, dv = 1000, 192, 128
+    n_kv, dv = 1000, 128
     g = torch.Generator(device=DEV)
     g.manual_seed(rows + hq)
     q = torch.ones((rows, hq, dqk), device=DEV, dtype=torch.bfloat16)
@@ -257,8 +260,9 @@ def test_huge_values_overflow_guard(rows, hq):
     (192, 128, "bf16", torch.float32, 4, 640, 2),     # 128-row workgroups
     (128, 128, "bf16", torch.bfloat16, 4, 640, 2),
     (192, 128, "bf16", torch.float32, 2, 2048, 128),  # 256-row workgroups
+    (128, 128, "bf16", torch.bfloat16, 2, 2048, 128),
     (64, 64, "f32", torch.float32, 4, 256, 4),        # fp32 kernel
-], ids=["192-f32acc", "128-bf16acc", "192-f32acc-256rows", "fp32"])
+], ids=["192-f32acc", "128-bf16acc", "192-f32acc-256rows", "128-bf16acc-256rows", "fp32"])
 def test_ring_accumulate_in_place(dqk, dv, dtype, odt, C, T, H):
     """Pass-Q style running accumulator: the C ring partials of a rank merged
     in the attention epilogue (accumulate=1), starting from an empty (LSE =
