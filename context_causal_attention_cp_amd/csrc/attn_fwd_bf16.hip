@@ -71,9 +71,14 @@ constexpr float kGrowMax = 64.0f;  // main mode: log2 headroom before the workgr
 constexpr float kMaxSum = 18446744073709551616.0f;  // 2^kGrowMax: largest accepted row sum
 constexpr int kNoPos = -(1 << 30);
 
-__device__ inline void map_work(int id, int num_tiles, int hq, int hkv, int &tile_order, int &h) {
+// workgroup id -> (query tile, first query head).  A KV head's G query heads
+// come in G / pack groups of pack heads (pack = 4 with GQA packing: the
+// workgroup's waves take its 4 heads over the same rows).
+__device__ inline void map_work(int id, int num_tiles, int hq, int hkv, int pack, int &tile_order,
+                                int &h) {
   const int G = hq / hkv;
-  const int per_kvh = num_tiles * G;
+  const int GP = G / pack;
+  const int per_kvh = num_tiles * GP;
   int kvh, rem;
   if (hkv % kNumXcd == 0) {
     const int x = id % kNumXcd, slot = id / kNumXcd;
@@ -83,8 +88,8 @@ __device__ inline void map_work(int id, int num_tiles, int hq, int hkv, int &til
     kvh = id / per_kvh;
     rem = id % per_kvh;
   }
-  tile_order = rem / G;
-  h = kvh * G + rem % G;
+  tile_order = rem / GP;
+  h = kvh * G + (rem % GP) * pack;
 }
 
 __device__ inline int find_seg(const LaunchSegs &L, int tile_order) {
@@ -347,17 +352,22 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   const int lane = tid & 63, n = lane & 31, hf = lane >> 5;
 
   int tile_order, h;
-  map_work(blockIdx.x, L.num_tiles, p.hq, p.hkv, tile_order, h);
+  map_work(blockIdx.x, L.num_tiles, p.hq, p.hkv, p.pack, tile_order, h);
   if (tile_order >= L.num_tiles) return;
   if (!EXACT) {
     if (tid == 0) s_flag = 0;
     __syncthreads();
   }
+  // GQA packing: every wave takes the same RW rows of its own query head
+  const bool packed = p.pack > 1;
+  const int BMr = packed ? RW : BM;    // query rows of the workgroup
+  const int wrow = packed ? 0 : w * RW;  // this wave's first row in them
+  if (packed) h += w;
   const SegDesc sd = L.s[find_seg(L, tile_order)];
-  const int ntile_q = (sd.q_len + BM - 1) / BM;
+  const int ntile_q = (sd.q_len + BMr - 1) / BMr;
   const int tq = ntile_q - 1 - (tile_order - sd.tile_begin);
-  const int row0 = tq * BM;
-  const int rows_here = min(BM, sd.q_len - row0);
+  const int row0 = tq * BMr;
+  const int rows_here = min(BMr, sd.q_len - row0);
   const int kvh = h / (p.hq / p.hkv);
 
   // ---- this lane's query rows (one per row block)
@@ -365,14 +375,14 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   bool valid[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int rr = w * RW + rb * 32 + n;
+    const int rr = wrow + rb * 32 + n;
     valid[rb] = rr < rows_here;
     qpos[rb] = valid[rb] ? sd.pos_begin + (row0 + rr) * sd.pos_stride : kNoPos;
   }
-  const int nvalid_w = max(0, min(RW, rows_here - w * RW));
-  const int qmin_w = nvalid_w ? sd.pos_begin + (row0 + w * RW) * sd.pos_stride : kNoPos;
+  const int nvalid_w = max(0, min(RW, rows_here - wrow));
+  const int qmin_w = nvalid_w ? sd.pos_begin + (row0 + wrow) * sd.pos_stride : kNoPos;
   const int qmax_w =
-      nvalid_w ? sd.pos_begin + (row0 + w * RW + nvalid_w - 1) * sd.pos_stride : kNoPos;
+      nvalid_w ? sd.pos_begin + (row0 + wrow + nvalid_w - 1) * sd.pos_stride : kNoPos;
   const int qmax_wg = sd.pos_begin + (row0 + rows_here - 1) * sd.pos_stride;
 
   // ---- tile counts: visible for the workgroup / this wave, fully visible
@@ -409,7 +419,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
   bf16x8 qf[RB][KS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int64_t qrow = (int64_t)sd.q_begin + row0 + w * RW + rb * 32 + n;
+    const int64_t qrow = (int64_t)sd.q_begin + row0 + wrow + rb * 32 + n;
     const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)h * p.q_hs + 8 * hf;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -754,7 +764,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
       }
     if (hf == 0) s_lse[w * 32 + n] = lse[rb];
     if (!p.accumulate && hf == 0 && valid[rb]) {
-      const int64_t orow = (int64_t)sd.o_begin + row0 + w * RW + rb * 32 + n;
+      const int64_t orow = (int64_t)sd.o_begin + row0 + wrow + rb * 32 + n;
       p.lse[orow * p.lse_rs + h] = lse[rb];
     }
     __builtin_amdgcn_s_barrier();  // (wave-local data; keeps the waves in step)
@@ -765,7 +775,7 @@ void attn_fwd_bf16_kernel(const AttnParams p, const LaunchSegs L) {
 #pragma unroll
     for (int r0 = 0; r0 < 32; r0 += RPI) {
       const int r = r0 + rsub;
-      const int rr = w * RW + rb * 32 + r;
+      const int rr = wrow + rb * 32 + r;
       if (rr < rows_here) {
         float4 a = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ);
         float4 c = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ + 16);
@@ -860,29 +870,34 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   const int lane = tid & 63, n = lane & 31, hf = lane >> 5;
 
   int tile_order, h;
-  map_work(blockIdx.x, L.num_tiles, p.hq, p.hkv, tile_order, h);
+  map_work(blockIdx.x, L.num_tiles, p.hq, p.hkv, p.pack, tile_order, h);
   if (tile_order >= L.num_tiles) return;
   if (tid == 0) s_flag = 0;
   __syncthreads();
+  // GQA packing: every wave pair takes the same 64 rows of its own query head
+  const bool packed = p.pack > 1;
+  const int BMr = packed ? RW : BM;    // query rows of the workgroup
+  const int wrow = packed ? 0 : s * RW;  // this wave pair's first row in them
+  if (packed) h += s;
   const SegDesc sd = L.s[find_seg(L, tile_order)];
-  const int ntile_q = (sd.q_len + BM - 1) / BM;
+  const int ntile_q = (sd.q_len + BMr - 1) / BMr;
   const int tq = ntile_q - 1 - (tile_order - sd.tile_begin);
-  const int row0 = tq * BM;
-  const int rows_here = min(BM, sd.q_len - row0);
+  const int row0 = tq * BMr;
+  const int rows_here = min(BMr, sd.q_len - row0);
   const int kvh = h / (p.hq / p.hkv);
 
   int qpos[RB];
   bool valid[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int rr = s * RW + rb * 32 + n;
+    const int rr = wrow + rb * 32 + n;
     valid[rb] = rr < rows_here;
     qpos[rb] = valid[rb] ? sd.pos_begin + (row0 + rr) * sd.pos_stride : kNoPos;
   }
-  const int nvalid_w = max(0, min(RW, rows_here - s * RW));
-  const int qmin_w = nvalid_w ? sd.pos_begin + (row0 + s * RW) * sd.pos_stride : kNoPos;
+  const int nvalid_w = max(0, min(RW, rows_here - wrow));
+  const int qmin_w = nvalid_w ? sd.pos_begin + (row0 + wrow) * sd.pos_stride : kNoPos;
   const int qmax_w =
-      nvalid_w ? sd.pos_begin + (row0 + s * RW + nvalid_w - 1) * sd.pos_stride : kNoPos;
+      nvalid_w ? sd.pos_begin + (row0 + wrow + nvalid_w - 1) * sd.pos_stride : kNoPos;
   const int qmax_wg = sd.pos_begin + (row0 + rows_here - 1) * sd.pos_stride;
 
   const int n_kv = sd.kv_len;
@@ -991,7 +1006,7 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
     bf16x8 qf[RB][KS];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int64_t qrow = (int64_t)sd.q_begin + row0 + s * RW + rb * 32 + n;
+      const int64_t qrow = (int64_t)sd.q_begin + row0 + wrow + rb * 32 + n;
       const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)h * p.q_hs + 8 * hf;
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
@@ -1250,7 +1265,7 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
       }
     if (hf == 0) s_lse[s * 32 + n] = lse[rb];
     if (!p.accumulate && hf == 0 && valid[rb]) {
-      const int64_t orow = (int64_t)sd.o_begin + row0 + s * RW + rb * 32 + n;
+      const int64_t orow = (int64_t)sd.o_begin + row0 + wrow + rb * 32 + n;
       p.lse[orow * p.lse_rs + h] = lse[rb];
     }
     constexpr int LPR = DV / 8;
@@ -1259,7 +1274,7 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
 #pragma unroll
     for (int r0 = 0; r0 < 32; r0 += RPI) {
       const int r = r0 + rsub;
-      const int rr = s * RW + rb * 32 + r;
+      const int rr = wrow + rb * 32 + r;
       if (rr < rows_here) {
         float4 a = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ);
         float4 c = *(const float4 *)(ost + r * OPITCH + sub * 8 * OSZ + 16);
@@ -1286,7 +1301,7 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
 // main pass, then the exact pass over the workgroups it flagged
 template <int DQK, int DV, int RB>
 hipError_t launch_rb(const AttnParams &p, const LaunchSegs &L, hipStream_t stream) {
-  const dim3 grid((unsigned)(L.num_tiles * p.hq));
+  const dim3 grid((unsigned)(L.num_tiles * p.hq / p.pack));
   // the split-role main pass for 256-row workgroups at qk 192 and 128
   // (measured 9-10 % faster than the one-wave kernel at both)
   if constexpr (RB == 2 && (DQK == 192 || DQK == 128))

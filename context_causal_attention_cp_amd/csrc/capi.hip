@@ -138,6 +138,7 @@ AttnParams make_params(const cp_attn_args &a) {
   p.causal = a.causal ? 1 : 0;
   p.o_bf16 = a.o_dtype == CP_BF16;
   p.accumulate = a.accumulate ? 1 : 0;
+  p.pack = 1;
   p.block_table = a.block_table;
   p.bt_stride = a.block_table_stride;
   p.block_size = a.block_size;
@@ -231,7 +232,8 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 // any partition of the keys).  Otherwise: 256-row workgroups, or 128-row
 // ones below kSmallGridWorkgroups, writing O and LSE directly.
 struct Bf16Plan {
-  int tile_rows = 0;
+  int tile_rows = 0;               // query rows x heads of one workgroup, in rows of one head
+  int pack = 1;                    // query heads per workgroup (GQA packing)
   int32_t parts = 0;               // > 0: split; parts per segment in seg_parts
   std::vector<int32_t> seg_parts;  // per caller segment
   std::vector<int32_t> seg_row;    // per caller segment: its first compact partial row
@@ -316,9 +318,16 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
     P.tile_rows = wgs_big < kSmallGridWorkgroups ? small : big;
     segs = plain_segs(a);
   }
-  P.launches = plan_launches(segs, P.tile_rows, a.causal != 0);
+  // GQA packing: when every KV head serves a multiple of 4 query heads, a
+  // workgroup takes 4 of them over tile_rows / 4 rows (each wave, or wave
+  // pair, one head of the same rows), so the 4 heads share each K/V tile in
+  // LDS and every wave sees the same key range ("What is Context
+  // Parallelism" blog, section 4.1: the query heads of a group read the same
+  // K and V)
+  P.pack = (a.hkv > 0 && a.hq % a.hkv == 0 && (a.hq / a.hkv) % 4 == 0) ? 4 : 1;
+  P.launches = plan_launches(segs, P.tile_rows / P.pack, a.causal != 0);
   int64_t wgs = 0;
-  for (const LaunchSegs &L : P.launches) wgs += static_cast<int64_t>(L.num_tiles) * a.hq;
+  for (const LaunchSegs &L : P.launches) wgs += static_cast<int64_t>(L.num_tiles) * a.hq / P.pack;
   // one int32 flag per workgroup of every launch (16-byte rounded; the
   // partials that follow start on a 256-byte boundary)
   P.flag_bytes = (static_cast<size_t>(wgs) * 4 + 15) / 16 * 16;
@@ -502,11 +511,12 @@ cp_status attn_fwd_impl(const cp_attn_args *a, void *ws_ptr, size_t ws_bytes, hi
     q.lse_rs = a->hq;
   }
   int32_t *flags = reinterpret_cast<int32_t *>(ws);
+  q.pack = P.pack;
   for (const LaunchSegs &L : P.launches) {
     q.ws = flags;
     const hipError_t e = launch_attn_bf16(q, L, a->dqk, a->dv, P.tile_rows, s);
     if (e != hipSuccess) return device_error(e);
-    flags += static_cast<int64_t>(L.num_tiles) * a->hq;
+    flags += static_cast<int64_t>(L.num_tiles) * a->hq / P.pack;
   }
   for (int32_t i = 0; i < a->num_segs && P.parts > 0; ++i) {
     const cp_segment &g = a->segs[i];

@@ -56,6 +56,8 @@ struct AttnParams {
   int32_t causal;
   int32_t o_bf16;     // 1: o is bf16, 0: fp32
   int32_t accumulate; // 1: merge into the (O, LSE) already in o / lse
+  int32_t pack;       // bf16 path: query heads of one KV head per workgroup (1, or 4:
+                      // one per wave (pair), the same rows; K/V tiles shared)
   const int32_t *block_table;  // paged KV, or null
   int64_t bt_stride;           // entries per request row
   int32_t block_size;          // rows per block

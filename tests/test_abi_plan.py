@@ -235,7 +235,11 @@ def test_attn_segment_errors():
 def test_workspace_size_query():
     # bf16: one int32 flag per workgroup; 2 segments of 4 rows x 4 heads = 8
     assert _ws() == (_lib.CP_OK, 32)
-    assert _ws(hq=8, hkv=2, q_row_stride=1024, o_row_stride=1024, lse_row_stride=8) == (_lib.CP_OK, 64)
+    # 8 query heads over 2 KV heads: GQA packing puts the 4 query heads of a
+    # KV head in one workgroup, so 2 segments x 2 head groups = 4 flags
+    assert _ws(hq=8, hkv=2, q_row_stride=1024, o_row_stride=1024, lse_row_stride=8) == (_lib.CP_OK, 16)
+    # 12 over 4 (3 per KV head): no packing, 2 x 12 flags
+    assert _ws(hq=12, hkv=4, q_row_stride=1536, o_row_stride=1536, lse_row_stride=12) == (_lib.CP_OK, 96)
     assert _ws(dtype=_lib.CP_F32, o_dtype=_lib.CP_F32) == (_lib.CP_OK, 0)
     assert _ws(hq=3)[0] == _lib.CP_ERR_ARG
 

@@ -34,6 +34,9 @@ CASES = [
     ("zigzag", 4, [256], [0], 4, 4, 64, 64, "f32"),
     ("interleave", 2, [70, 131], [3, 40], 4, 2, 128, 128, "f32"),
     ("zigzag", 1, [190], [0], 2, 1, 128, 128, "bf16"),
+    # GQA packing (4 query heads of one KV head per workgroup): 4 and 8 per group
+    ("zigzag", 2, [700, 45], [60, 0], 16, 4, 192, 128, "bf16"),
+    ("interleave", 3, [260, 1, 515], [0, 30, 7], 8, 1, 128, 128, "bf16"),
 ]
 
 
@@ -174,16 +177,18 @@ def test_repeatable_bitwise():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-GROWTH = [(300, 4, 0.1, 1, 192), (300, 4, 0.5, 1, 192), (4096, 128, 0.5, 1, 192),
-          (300, 4, 0.36, 1, 192), (4096, 128, 0.23, 2, 192), (4096, 128, 0.146, 1, 128),
-          (4096, 128, 0.5415, 1, 128)]
+GROWTH = [(300, 4, 4, 0.1, 1, 192), (300, 4, 4, 0.5, 1, 192), (4096, 128, 128, 0.5, 1, 192),
+          (300, 4, 4, 0.36, 1, 192), (4096, 128, 128, 0.23, 2, 192),
+          (4096, 128, 128, 0.146, 1, 128), (4096, 128, 128, 0.5415, 1, 128),
+          (300, 8, 2, 0.36, 1, 192), (4096, 128, 32, 0.5, 1, 192), (4096, 64, 16, 0.146, 1, 128)]
 GROWTH_IDS = ["small-2^27", "small-2^138", "large-2^138", "small-2^100", "large-2x2^63.6",
-              "large-d128-2^27", "large-d128-2^100"]
+              "large-d128-2^27", "large-d128-2^100", "small-gqa-2^100", "large-gqa-2^138",
+              "large-gqa-d128-2^27"]
 
 
 @pytest.mark.parametrize("accumulate", [False, True], ids=["write", "accumulate"])
-@pytest.mark.parametrize("rows,hq,val,nbig,dqk", GROWTH, ids=GROWTH_IDS)
-def test_reference_growth(rows, hq, val, nbig, dqk, accumulate):
+@pytest.mark.parametrize("rows,hq,hkv,val,nbig,dqk", GROWTH, ids=GROWTH_IDS)
+def test_reference_growth(rows, hq, hkv, val, nbig, dqk, accumulate):
     """Keys, in a late tile, far above every score of the first tile: with
     q = 1 and keys 0 except keys 900.. = val (d dims, scale 1) the row max
     grows by d*val*log2(e) in log2 units -- 2^27 (kept by the main pass),
@@ -195,15 +200,20 @@ def test_reference_growth(rows, hq, val, nbig, dqk, accumulate):
     accumulate: keys 0..449 are first written by a plain call, then keys
     450..999 (with the large ones) are merged into that running (O, LSE) by
     an accumulating call; a flagged workgroup must merge exactly once (in
-    the exact pass), which the dense result over all keys checks."""
+    the exact pass), which the dense result over all keys checks.
+    hkv < hq: GQA packing puts 4 query heads of one KV head in a workgroup;
+    every fourth query head has q = 0 (no growth), so a flagged workgroup
+    holds heads that would not have been flagged on their own."""
     n_kv, dv = 1000, 128
     g = torch.Generator(device=DEV)
     g.manual_seed(rows + hq)
     q = torch.ones((rows, hq, dqk), device=DEV, dtype=torch.bfloat16)
-    k = torch.zeros((n_kv, hq, dqk), device=DEV, dtype=torch.bfloat16)
+    if hkv < hq:
+        q[:, 1::4] = 0
+    k = torch.zeros((n_kv, hkv, dqk), device=DEV, dtype=torch.bfloat16)
     k[900:900 + nbig] = val
-    v = torch.randn((n_kv, hq, dv), generator=g, device=DEV).to(torch.bfloat16)
-    say(f"reference growth rows={rows} hq={hq} val={val} keys={nbig} accumulate={accumulate}")
+    v = torch.randn((n_kv, hkv, dv), generator=g, device=DEV).to(torch.bfloat16)
+    say(f"reference growth rows={rows} hq={hq} hkv={hkv} val={val} keys={nbig} accumulate={accumulate}")
     if not accumulate:
         # every row sees all keys (positions n_kv .. n_kv + rows - 1)
         segs = [cp.Segment(0, 0, rows, n_kv, 1, 0, n_kv)]
@@ -218,8 +228,9 @@ def test_reference_growth(rows, hq, val, nbig, dqk, accumulate):
     torch.cuda.synchronize()
     sample = sorted(set([0, 1, rows // 2, rows - 1]))
     q64, k64, v64 = f64(q), f64(k), f64(v)
-    for h in sorted(set([0, hq - 1])):
-        ro, rl = ao.attend(q64[sample, h], k64[:, h], v64[:, h], [n_kv + i for i in sample],
+    for h in sorted(set([0, 1, hq - 1])):
+        kh = h // (hq // hkv)
+        ro, rl = ao.attend(q64[sample, h], k64[:, kh], v64[:, kh], [n_kv + i for i in sample],
                            np.arange(n_kv), 1.0)
         compare(f64(o[sample, h]), f64(lse[sample, h]), ro, rl, range(len(sample)), "bf16",
                 f"head {h}")
@@ -256,19 +267,22 @@ def test_huge_values_overflow_guard(rows, hq):
                 "bf16", f"head {h} (O / 2^70)")
 
 
-@pytest.mark.parametrize("dqk,dv,dtype,odt,C,T,H", [
-    (192, 128, "bf16", torch.float32, 4, 640, 2),     # 128-row workgroups
-    (128, 128, "bf16", torch.bfloat16, 4, 640, 2),
-    (192, 128, "bf16", torch.float32, 2, 2048, 128),  # 256-row workgroups
-    (128, 128, "bf16", torch.bfloat16, 2, 2048, 128),
-    (64, 64, "f32", torch.float32, 4, 256, 4),        # fp32 kernel
-], ids=["192-f32acc", "128-bf16acc", "192-f32acc-256rows", "128-bf16acc-256rows", "fp32"])
-def test_ring_accumulate_in_place(dqk, dv, dtype, odt, C, T, H):
+@pytest.mark.parametrize("dqk,dv,dtype,odt,C,T,H,HK", [
+    (192, 128, "bf16", torch.float32, 4, 640, 2, 2),       # 128-row workgroups
+    (128, 128, "bf16", torch.bfloat16, 4, 640, 2, 2),
+    (192, 128, "bf16", torch.float32, 2, 2048, 128, 128),  # 256-row workgroups
+    (128, 128, "bf16", torch.bfloat16, 2, 2048, 128, 128),
+    (192, 128, "bf16", torch.float32, 2, 2048, 128, 32),   # GQA packing, 4 heads x 64 rows
+    (128, 128, "bf16", torch.bfloat16, 2, 2048, 64, 8),
+    (64, 64, "f32", torch.float32, 4, 256, 4, 4),          # fp32 kernel
+], ids=["192-f32acc", "128-bf16acc", "192-f32acc-256rows", "128-bf16acc-256rows",
+        "192-f32acc-gqa-packed", "128-bf16acc-gqa-packed", "fp32"])
+def test_ring_accumulate_in_place(dqk, dv, dtype, odt, C, T, H, HK):
     """Pass-Q style running accumulator: the C ring partials of a rank merged
     in the attention epilogue (accumulate=1), starting from an empty (LSE =
     -inf) accumulator, must equal the dense attention of the rank's rows;
     partial calls whose rows see no key leave the accumulator untouched."""
-    q, k, v = _tensors(T, T, H, H, dqk, dv, dtype, seed=dqk + C)
+    q, k, v = _tensors(T, T, H, HK, dqk, dv, dtype, seed=dqk + C)
     q64, k64, v64 = f64(q), f64(k), f64(v)
     scale = 1.0 / np.sqrt(dqk)
     for r in sorted({0, C - 1}):
@@ -287,6 +301,6 @@ def test_ring_accumulate_in_place(dqk, dv, dtype, odt, C, T, H):
                         kv_pos=idx.to(torch.int32), o=o, lse=lse, accumulate=True)
         torch.cuda.synchronize()
         dense_o, dense_l = ao.shard_attention(q64[mine], k64, v64,
-                                              oracle_segments("zigzag", C, r, [T], [0]), H, H, scale)
+                                              oracle_segments("zigzag", C, r, [T], [0]), H, HK, scale)
         compare(f64(o), f64(lse), dense_o, dense_l, range(len(mine)),
                 "bf16" if dtype == "bf16" else "f32", f"rank {r} accumulated")
