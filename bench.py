@@ -357,7 +357,7 @@ def _restore(cp, w, k):
     torch.cuda.empty_cache()
     return {"ms": round(ms, 4), "algorithmic_bytes": by, "GB/s": round(by / ms / 1e6, 1),
             "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
-            "traffic": _profiled_traffic("restore_apply_kernel", "restore_apply.hip")}
+            "traffic": _profiled_traffic("restore_apply_long_kernel", "restore_apply.hip")}
 
 
 def _direct(cp, w, q_loc, k, v, plan):

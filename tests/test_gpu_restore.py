@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.mark.parametrize("rows,row_elems", [(37, 8), (300, 24), (1000, 136), (65, 24576)])
+@pytest.mark.parametrize("rows,row_elems", [(37, 8), (300, 24), (1000, 136), (50, 400), (129, 2072),
+                                           (65, 24576)])
 def test_restore_apply_random(rows, row_elems):
     say(f"restore apply rows={rows} row_bytes={row_elems * 2}")
     g = torch.Generator(device=DEV)
