@@ -214,10 +214,16 @@ std::vector<LaunchSegs> plan_launches(const std::vector<PlanSeg> &segs, int tile
 // Below this many workgroups a bf16 call is too small to fill the 256
 // compute units well.
 constexpr int64_t kSmallGridWorkgroups = 512;
-// Split calls: aim for this many workgroups, with key chunks of at least
-// kMinSplitKeys keys and at most kMaxSplitParts chunks per segment.
-constexpr int64_t kSplitTargetWorkgroups = 1024;
-constexpr int64_t kMinSplitKeys = 1024;
+// Split calls: the key chunk size comes from a model of the launch.  W
+// workgroups of 256 rows (one per compute unit: their LDS fills it) run in
+// ceil(W / kComputeUnits) rounds, each as long as its longest workgroup: its
+// key tiles plus a fixed cost of kWorkgroupFixedTiles tiles (Q load, the
+// pipeline's fill and drain, the epilogue; measured on MI355X at qk 128:
+// 1.0 us per 32-key tile and 12-13 us per workgroup).  Chunks have at least
+// kMinSplitKeys keys, a segment at most kMaxSplitParts of them.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kWorkgroupFixedTiles = 12;
+constexpr int64_t kMinSplitKeys = 256;
 constexpr int32_t kMaxSplitParts = 16;
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -247,14 +253,13 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
   Bf16Plan P;
   const int small = attn_bf16_tile_rows(a.dqk, a.dv, true);
   const int big = attn_bf16_tile_rows(a.dqk, a.dv, false);
-  int64_t wgs_small = 0, wgs_big = 0, work = 0, max_kv = 0;
+  int64_t wgs_small = 0, wgs_big = 0, max_kv = 0;
   for (int32_t i = 0; i < a.num_segs; ++i) {
     const cp_segment &g = a.segs[i];
     const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
     if (nq <= 0 || nk <= 0) continue;
     wgs_small += (nq + small - 1) / small * a.hq;
     wgs_big += (nq + big - 1) / big * a.hq;
-    work += (nq + big - 1) / big * a.hq * nk;
     max_kv = std::max(max_kv, nk);
   }
   // the merge writes whole (row, head) runs: dense O and LSE rows only
@@ -265,11 +270,51 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
   // kMaxSplitParts x rows stays far inside int32)
   const bool can_split = !a.accumulate && !a.block_table && dense &&
                          wgs_small < kSmallGridWorkgroups && max_kv <= (1 << 28);
+  // GQA packing: when every KV head serves a multiple of 4 query heads, a
+  // workgroup takes 4 of them over tile_rows / 4 rows (each wave, or wave
+  // pair, one head of the same rows), so the 4 heads share each K/V tile in
+  // LDS and every wave sees the same key range ("What is Context
+  // Parallelism" blog, section 4.1: the query heads of a group read the same
+  // K and V)
+  P.pack = (a.hkv > 0 && a.hq % a.hkv == 0 && (a.hq / a.hkv) % 4 == 0) ? 4 : 1;
   std::vector<PlanSeg> segs;
   if (can_split) {
-    int64_t chunk = std::max<int64_t>(kMinSplitKeys, (work + kSplitTargetWorkgroups - 1) /
-                                                         kSplitTargetWorkgroups);
-    chunk = (chunk + 31) / 32 * 32;
+    // the chunk size with the shortest modelled launch, among those that cut
+    // some segment into 1 .. kMaxSplitParts equal whole-tile parts
+    auto tiles32 = [](int64_t x) { return (x + 31) / 32 * 32; };
+    auto parts_of = [](int64_t nk, int64_t c) {
+      return std::min<int64_t>(kMaxSplitParts, (nk + c - 1) / c);
+    };
+    const int64_t rows_wg = big / P.pack, groups = a.hq / P.pack;
+    std::vector<int64_t> cands;
+    for (int32_t i = 0; i < a.num_segs; ++i) {
+      const int64_t nk = a.segs[i].kv_end - a.segs[i].kv_begin;
+      if (a.segs[i].q_end <= a.segs[i].q_begin || nk <= 0) continue;
+      for (int64_t np = 1; np <= kMaxSplitParts; ++np) {
+        const int64_t c = tiles32((nk + np - 1) / np);
+        if (np == 1 || c >= kMinSplitKeys) cands.push_back(c);
+      }
+    }
+    std::sort(cands.begin(), cands.end());
+    cands.erase(std::unique(cands.begin(), cands.end()), cands.end());
+    int64_t chunk = 0, best_est = 0, best_wgs = 0;
+    for (const int64_t c : cands) {
+      int64_t wgs = 0, tiles = 0;
+      for (int32_t i = 0; i < a.num_segs; ++i) {
+        const cp_segment &g = a.segs[i];
+        const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
+        if (nq <= 0 || nk <= 0) continue;
+        const int64_t np = parts_of(nk, c);
+        wgs += np * ((nq + rows_wg - 1) / rows_wg) * groups;
+        tiles = std::max(tiles, tiles32((nk + np - 1) / np) / 32);
+      }
+      const int64_t est = (wgs + kComputeUnits - 1) / kComputeUnits * (tiles + kWorkgroupFixedTiles);
+      if (chunk == 0 || est < best_est || (est == best_est && wgs < best_wgs)) {
+        chunk = c;
+        best_est = est;
+        best_wgs = wgs;
+      }
+    }
     P.seg_parts.assign(a.num_segs, 0);
     P.seg_row.assign(a.num_segs, 0);
     // partial rows are compact: the rows of the split segments, numbered in
@@ -285,8 +330,8 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
       const cp_segment &g = a.segs[i];
       const int64_t nq = g.q_end - g.q_begin, nk = g.kv_end - g.kv_begin;
       if (nq <= 0 || nk <= 0) continue;
-      const int64_t np = std::min<int64_t>(kMaxSplitParts, (nk + chunk - 1) / chunk);
-      const int64_t c = ((nk + np - 1) / np + 31) / 32 * 32;  // whole tiles per chunk
+      const int64_t np = parts_of(nk, chunk);
+      const int64_t c = tiles32((nk + np - 1) / np);  // whole tiles per chunk
       int32_t made = 0;
       for (int64_t off = 0; off < nk; off += c, ++made) {
         PlanSeg ps{g, 0};
@@ -318,13 +363,6 @@ Bf16Plan plan_bf16(const cp_attn_args &a) {
     P.tile_rows = wgs_big < kSmallGridWorkgroups ? small : big;
     segs = plain_segs(a);
   }
-  // GQA packing: when every KV head serves a multiple of 4 query heads, a
-  // workgroup takes 4 of them over tile_rows / 4 rows (each wave, or wave
-  // pair, one head of the same rows), so the 4 heads share each K/V tile in
-  // LDS and every wave sees the same key range ("What is Context
-  // Parallelism" blog, section 4.1: the query heads of a group read the same
-  // K and V)
-  P.pack = (a.hkv > 0 && a.hq % a.hkv == 0 && (a.hq / a.hkv) % 4 == 0) ? 4 : 1;
   P.launches = plan_launches(segs, P.tile_rows / P.pack, a.causal != 0);
   int64_t wgs = 0;
   for (const LaunchSegs &L : P.launches) wgs += static_cast<int64_t>(L.num_tiles) * a.hq / P.pack;

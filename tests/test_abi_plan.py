@@ -203,11 +203,12 @@ def test_attn_arg_errors(kw, want):
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch():
-    # one long segment, 4 heads: few enough workgroups that the keys are split,
-    # fp32 partials of 16000 rows x 4 heads x 128 need more than the static
-    # scratch; the call must say so and enqueue nothing (no device is touched)
-    segs = (_lib.Segment * 1)(_lib.Segment(0, 0, 16000, (1 << 20) - 16000, 1, 0, 1 << 20))
-    kw = dict(num_q_rows=16000, num_kv_rows=1 << 20, hq=4, hkv=4, o_dtype=_lib.CP_F32,
+    # one long segment, 4 heads: 112 workgroups of 256 rows, so the 2^20 keys
+    # are cut into 16 chunks (7 rounds of workgroups); fp32 partials of
+    # 16 x 7168 rows x 4 heads x 128 need more than the static scratch; the
+    # call must say so and enqueue nothing (no device is touched)
+    segs = (_lib.Segment * 1)(_lib.Segment(0, 0, 7168, (1 << 20) - 7168, 1, 0, 1 << 20))
+    kw = dict(num_q_rows=7168, num_kv_rows=1 << 20, hq=4, hkv=4, o_dtype=_lib.CP_F32,
               k_row_stride=512, v_row_stride=512, num_segs=1, segs=segs)
     st, need = _ws(**kw)
     assert st == _lib.CP_OK and need > _lib.NOALLOC_SCRATCH_BYTES
@@ -245,22 +246,27 @@ def test_workspace_size_query():
 
 
 def test_split_workspace_size():
-    # one 512-row causal segment against 8192 keys, 32 heads, bf16 out: 4 x 32
-    # 128-row workgroups (< 512), so the keys are cut into 8 chunks of 1024 and
-    # every chunk is a 2 x 32-workgroup launch segment writing a partial:
-    # flags 8 x 64 x 4 B + partial O 8 x 512 x 32 x 128 x 2 B + LSE 8 x 512 x 32 x 4 B
+    # one 512-row causal segment against 8192 keys, 32 heads over 8 KV heads,
+    # bf16 out: 4 x 32 128-row workgroups (< 512), so the keys are split.  With
+    # GQA packing a workgroup takes 64 rows x 4 heads: 8 x 8 per chunk, and the
+    # launch model picks 4 chunks of 2048 keys (256 workgroups, one round):
+    # flags 4 x 64 x 4 B + partial O 4 x 512 x 32 x 128 x 2 B + LSE 4 x 512 x 32 x 4 B
     segs = (_lib.Segment * 1)(_lib.Segment(0, 0, 512, 7680, 1, 0, 8192))
     kw = dict(num_q_rows=512, num_kv_rows=8192, hq=32, hkv=8, q_row_stride=32 * 128,
               k_row_stride=8 * 128, v_row_stride=8 * 128, o_row_stride=32 * 128,
               lse_row_stride=32, segs=segs, num_segs=1)
-    split_bytes = 2048 + 8 * 512 * 32 * 128 * 2 + 8 * 512 * 32 * 4
+    split_bytes = 1024 + 4 * 512 * 32 * 128 * 2 + 4 * 512 * 32 * 4
     assert _ws(**kw) == (_lib.CP_OK, split_bytes)
     # partial rows cover only the segments' rows, not the whole output buffer
     assert _ws(**dict(kw, num_q_rows=100000)) == (_lib.CP_OK, split_bytes)
     # non-dense output rows: no split, flags of the 4 x 32 128-row workgroups only
     assert _ws(**dict(kw, o_row_stride=32 * 128 + 8)) == (_lib.CP_OK, 512)
-    # short keys: nothing to split
-    short = (_lib.Segment * 1)(_lib.Segment(0, 0, 512, 0, 1, 0, 1000))
+    # 1000 keys: 4 chunks of 256 (8 tiles each, against 32 unsplit)
+    k1000 = (_lib.Segment * 1)(_lib.Segment(0, 0, 512, 488, 1, 0, 1000))
+    assert _ws(**dict(kw, segs=k1000)) == (
+        _lib.CP_OK, 1024 + 4 * 512 * 32 * 128 * 2 + 4 * 512 * 32 * 4)
+    # short keys (under two chunks of the 256-key minimum): nothing to split
+    short = (_lib.Segment * 1)(_lib.Segment(0, 0, 512, 0, 1, 0, 400))
     assert _ws(**dict(kw, segs=short)) == (_lib.CP_OK, 512)
     # accumulate mode never splits
     assert _ws(**dict(kw, accumulate=1)) == (_lib.CP_OK, 512)

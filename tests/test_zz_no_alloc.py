@@ -91,13 +91,14 @@ def test_noalloc_decode():
 
 
 def test_noalloc_too_large_is_refused():
-    # same split shape as above but fp32 partials over 16000 rows x 4 heads:
-    # more than the static scratch; nothing may be enqueued or written
-    q = torch.zeros((16000, 4, 128), device=DEV, dtype=torch.bfloat16)
+    # 7168 rows x 4 heads against 2^20 keys: 112 workgroups of 256 rows, so the
+    # keys are cut into 16 chunks, whose fp32 partials (235 MB) are more than
+    # the static scratch; nothing may be enqueued or written
+    q = torch.zeros((7168, 4, 128), device=DEV, dtype=torch.bfloat16)
     k = torch.zeros((1 << 20, 4, 128), device=DEV, dtype=torch.bfloat16)
-    o = torch.full((16000, 4, 128), 5.0, device=DEV)
-    lse = torch.full((16000, 4), 5.0, device=DEV)
-    segs = [cp.Segment(0, 0, 16000, (1 << 20) - 16000, 1, 0, 1 << 20)]
+    o = torch.full((7168, 4, 128), 5.0, device=DEV)
+    lse = torch.full((7168, 4), 5.0, device=DEV)
+    segs = [cp.Segment(0, 0, 7168, (1 << 20) - 7168, 1, 0, 1 << 20)]
     with pytest.raises(cp.CpError) as e:
         cp.attn_fwd_noalloc(q, k, k, segs, 0.1, o, lse)
     assert e.value.status == 3
