@@ -556,18 +556,33 @@ cp_status attn_fwd_impl(const cp_attn_args *a, void *ws_ptr, size_t ws_bytes, hi
     if (e != hipSuccess) return device_error(e);
     flags += static_cast<int64_t>(L.num_tiles) * a->hq / P.pack;
   }
-  for (int32_t i = 0; i < a->num_segs && P.parts > 0; ++i) {
-    const cp_segment &g = a->segs[i];
-    const int32_t np = P.seg_parts[i];
-    if (np == 0) continue;
-    const int64_t src = static_cast<int64_t>(P.seg_row[i]) * a->hq;  // first (row, head) pair
-    const int64_t dst = static_cast<int64_t>(g.q_begin) * a->hq;
-    const size_t elt = o_bf16 ? 2 : 4;
-    const hipError_t e = launch_lse_merge(
-        np, static_cast<int64_t>(g.q_end - g.q_begin) * a->hq, a->dv,
-        static_cast<const char *>(q.o) + src * a->dv * elt, o_bf16, part_rows * a->dv,
-        q.lse + src, part_rows, static_cast<char *>(a->o) + dst * a->dv * elt, o_bf16,
-        a->lse + dst, s);
+  // the split segments' merges, up to kMaxMergeSegs per launch
+  if (P.parts > 0) {
+    const int64_t ppw = lse_merge_pairs_per_workgroup(a->dv);
+    MergeSegs T{};
+    auto flush = [&]() -> hipError_t {
+      if (T.n == 0) return hipSuccess;
+      const hipError_t e = launch_lse_merge_segs(T, a->dv, q.o, o_bf16, part_rows, q.lse, a->o,
+                                                 o_bf16, a->lse, s);
+      T = MergeSegs{};
+      return e;
+    };
+    for (int32_t i = 0; i < a->num_segs; ++i) {
+      const cp_segment &g = a->segs[i];
+      const int32_t np = P.seg_parts[i];
+      if (np == 0) continue;
+      const int64_t pairs = static_cast<int64_t>(g.q_end - g.q_begin) * a->hq;
+      T.parts[T.n] = np;
+      T.pairs[T.n] = pairs;
+      T.src[T.n] = static_cast<int64_t>(P.seg_row[i]) * a->hq;  // first (row, head) pair
+      T.dst[T.n] = static_cast<int64_t>(g.q_begin) * a->hq;
+      T.wg_begin[T.n + 1] = T.wg_begin[T.n] + static_cast<int32_t>((pairs + ppw - 1) / ppw);
+      if (++T.n == kMaxMergeSegs) {
+        const hipError_t e = flush();
+        if (e != hipSuccess) return device_error(e);
+      }
+    }
+    const hipError_t e = flush();
     if (e != hipSuccess) return device_error(e);
   }
   return fill_empty_segments(a, s);

@@ -110,6 +110,25 @@ hipError_t launch_restore_apply(const int32_t *index, int64_t n, const void *src
                                 int64_t src_stride, void *dst, int64_t dst_stride,
                                 int64_t row_bytes, hipStream_t stream);
 
+// Several independent LSE merges in one launch (the key-split segments of an
+// attention call).  Segment i: `parts[i]` partials of `pairs[i]` (row, head)
+// pairs; partial j of its pair x at pair index j * part_stride + src[i] + x
+// of the partial buffers, its output at pair index dst[i] + x; it owns
+// workgroups wg_begin[i] .. wg_begin[i + 1] - 1, one per
+// lse_merge_pairs_per_workgroup(dv) pairs.
+constexpr int kMaxMergeSegs = 64;
+struct MergeSegs {
+  int32_t n;
+  int32_t wg_begin[kMaxMergeSegs + 1];
+  int32_t parts[kMaxMergeSegs];
+  int64_t pairs[kMaxMergeSegs];
+  int64_t src[kMaxMergeSegs];
+  int64_t dst[kMaxMergeSegs];
+};
+int lse_merge_pairs_per_workgroup(int32_t dv);
+hipError_t launch_lse_merge_segs(const MergeSegs &T, int32_t dv, const void *o_parts,
+                                 int part_bf16, int64_t part_stride, const float *lse_parts,
+                                 void *o_out, int out_bf16, float *lse_out, hipStream_t stream);
 hipError_t launch_lse_merge(int32_t parts, int64_t pairs, int32_t dv,
                             const void *o_parts, int part_bf16,
                             int64_t o_part_stride, const float *lse_parts,
