@@ -971,7 +971,9 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   };
   // iteration i begins: this wave's part of tile i has landed and its LDS
   // operations of iteration i - 1 are done; after the barrier every wave has
-  // all of tile i and P(i - 2) of every score wave
+  // all of tile i and P(i - 2) of every score wave.  The score waves then
+  // issue their part of tile i + PREF; the output waves issue theirs after
+  // their products (their products start sooner: 2-3 % faster)
   auto top = [&](int i) {
     const int later = min(n_wg - 1 - i, PREF - 1);
     if (score) {
@@ -981,7 +983,7 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
       wait_later_lgkm0<C::VDMA, PREF - 1>(later);
     }
     __builtin_amdgcn_s_barrier();
-    if (i + PREF < n_wg) issue(i + PREF);
+    if (score && i + PREF < n_wg) issue(i + PREF);
   };
   auto stage = [&](int t) { return (const char *)sm[t % NBUF]; };
 
@@ -1219,6 +1221,7 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   for (int i = 0; i < n_wg + 2; ++i) {
     top(i);
     if (i >= 3 && i - 3 < n_vis) pv_products();
+    if (i + PREF < n_wg) issue(i + PREF);
     if (i >= 2 && i - 2 < n_vis) pv_reads(i - 2);
   }
   if (n_wg >= 1 && n_wg - 1 < n_vis) {  // the last tile, read in the last iteration
