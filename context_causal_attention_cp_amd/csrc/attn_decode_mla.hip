@@ -571,15 +571,21 @@ void attn_decode_px_kernel(const AttnParams p, const DecodeLaunch D) {
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)kbase, (short)0, (int)((int64_t)k_hi * p.k_rs * 2), 0x00020000);
   const int x_lo = sd.kv_begin + k_lo;  // paged: first logical row of the slice
-  auto tile_rsrc = [&](int t, uint32_t &row0) -> __amdgpu_buffer_rsrc_t {
+  // paged: the pool block of tile t (its 32 rows sit in one block; clamped
+  // into the pool).  Looked up ahead of the DMA issue: the scalar load's
+  // wait would otherwise also wait for every LDS operation in flight.
+  auto tile_block = [&](int t) -> int {
+    if (!PAGED) return 0;
+    const int x0 = x_lo + t * BN;
+    const int b = p.block_table[(int64_t)sd.req * p.bt_stride + x0 / p.block_size];
+    return __builtin_amdgcn_readfirstlane(min(max(b, 0), p.pool_blocks - 1));
+  };
+  auto tile_rsrc = [&](int t, int b, uint32_t &row0) -> __amdgpu_buffer_rsrc_t {
     if (!PAGED) {
       row0 = (uint32_t)((k_lo + t * BN) * p.k_rs) * 2u;
       return krsrc;
     }
-    // the tile's 32 rows sit in one block (clamped into the pool)
     const int x0 = x_lo + t * BN;
-    int b = p.block_table[(int64_t)sd.req * p.bt_stride + x0 / p.block_size];
-    b = __builtin_amdgcn_readfirstlane(min(max(b, 0), p.pool_blocks - 1));
     const int64_t prow = (int64_t)b * p.block_size + x0 % p.block_size;
     const int rows = min(BN, k_hi - (k_lo + t * BN));
     row0 = 0u;
@@ -594,9 +600,9 @@ void attn_decode_px_kernel(const AttnParams p, const DecodeLaunch D) {
   uint32_t dma_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dma_off[i] = dma_lane_offset(wi0 + i, lane, (int)p.k_rs);
-  auto issue = [&](int t) {
+  auto issue = [&](int t, int b) {
     uint32_t row0;
-    const __amdgpu_buffer_rsrc_t trsrc = tile_rsrc(t, row0);
+    const __amdgpu_buffer_rsrc_t trsrc = tile_rsrc(t, b, row0);
     u32x4 *dst = lds + (t % NBUF_X) * TILE_CH;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -680,9 +686,10 @@ void attn_decode_px_kernel(const AttnParams p, const DecodeLaunch D) {
     }
   };
 
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
+  if (ntiles > 0) issue(0, tile_block(0));
+  if (ntiles > 1) issue(1, tile_block(1));
   for (int t = 0; t < ntiles; ++t) {
+    const int bnext = t + 2 < ntiles ? tile_block(t + 2) : 0;
     // tile t has landed (only tile t + 1 may still be in flight) and this
     // wave's P(t - 1) is written; after the barrier every wave has both
     if (t + 1 < ntiles) {
@@ -690,11 +697,12 @@ void attn_decode_px_kernel(const AttnParams p, const DecodeLaunch D) {
     } else {
       wait_vm_lgkm0<0>();
     }
+    if (PAGED) asm volatile("" : : "s"(bnext));  // the block id is in by now
     __builtin_amdgcn_s_barrier();
     if (t > 0) pv(t - 1);
     // tile t + 2 goes to the stage of tile t - 2, free since the barrier;
     // issued after the PV step rather than before it: 8 % faster
-    if (t + 2 < ntiles) issue(t + 2);
+    if (t + 2 < ntiles) issue(t + 2, bnext);
     // ---- S^T = K Q^T of tile t for this wave's heads, their numerators
     // against the fixed reference, written to P buffer t & 1
     // a scheduling region of its own: the products of the PV step above
