@@ -935,6 +935,11 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   const uint32_t k_lane = (uint32_t)(lane & 15) * k_rb + (uint32_t)(lane >> 4) * 16u;
   const uint32_t v_lane =
       (uint32_t)(4 * ((lane >> 2) / VCH) + (lane & 3)) * v_rb + (uint32_t)((lane >> 2) % VCH) * 16u;
+  // Who copies a tile: at qk 192 the score waves copy K (and the key
+  // positions) right after the barrier and the output waves V after their
+  // products; at qk 128 the score waves copy the whole tile right after the
+  // barrier (measured: 2-3 % faster there, no faster at qk 192)
+  constexpr bool S_ALL = DQK == 128;
   auto issue = [&](int t) {
     const int j0 = t * BN;
     const int nrows = min(BN, n_kv - j0);
@@ -956,7 +961,8 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
             pr, (__attribute__((address_space(3))) void *)(dst + C::KPOS), 4, lane_id_here() * 4u,
             0, 0, 0);
       }
-    } else {
+    }
+    if (score == S_ALL) {
       const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(vbase + (int64_t)j0 * p.v_rs), (short)0, (int)(nrows * v_rb), 0x00020000);
 #pragma unroll
@@ -972,15 +978,16 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   // iteration i begins: this wave's part of tile i has landed and its LDS
   // operations of iteration i - 1 are done; after the barrier every wave has
   // all of tile i and P(i - 2) of every score wave.  The score waves then
-  // issue their part of tile i + PREF; the output waves issue theirs after
-  // their products (their products start sooner: 2-3 % faster)
+  // issue their part of tile i + PREF; the output waves issue theirs (qk 192)
+  // after their products, which then start sooner (2-3 % faster)
   auto top = [&](int i) {
     const int later = min(n_wg - 1 - i, PREF - 1);
+    constexpr int SPER = C::KDMA + (S_ALL ? C::VDMA : 0);  // score wave's DMA per tile
     if (score) {
-      if (kvp && s == 0) wait_later_lgkm0<C::KDMA + 1, PREF - 1>(later);
-      else wait_later_lgkm0<C::KDMA, PREF - 1>(later);
+      if (kvp && s == 0) wait_later_lgkm0<SPER + 1, PREF - 1>(later);
+      else wait_later_lgkm0<SPER, PREF - 1>(later);
     } else {
-      wait_later_lgkm0<C::VDMA, PREF - 1>(later);
+      wait_later_lgkm0<S_ALL ? 0 : C::VDMA, PREF - 1>(later);
     }
     __builtin_amdgcn_s_barrier();
     if (score && i + PREF < n_wg) issue(i + PREF);
@@ -1221,7 +1228,7 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   for (int i = 0; i < n_wg + 2; ++i) {
     top(i);
     if (i >= 3 && i - 3 < n_vis) pv_products();
-    if (i + PREF < n_wg) issue(i + PREF);
+    if (!S_ALL && i + PREF < n_wg) issue(i + PREF);
     if (i >= 2 && i - 2 < n_vis) pv_reads(i - 2);
   }
   if (n_wg >= 1 && n_wg - 1 < n_vis) {  // the last tile, read in the last iteration
