@@ -825,7 +825,9 @@ struct SplitCfg {
   using C = Cfg<DQK, DV>;
   static constexpr int PBYTES = 2 * 4 * 4096;
   static constexpr int NBUF_FIT = (160 * 1024 - PBYTES - 3 * 1024) / (C::STAGE * 16);
-  static constexpr int NBUF = NBUF_FIT < 8 ? NBUF_FIT : 8;
+  // five stages, two tiles in flight beyond the three being read: measured
+  // faster than six to eight (0.5 % at qk 192, 3-4 % at qk 128)
+  static constexpr int NBUF = NBUF_FIT < 5 ? NBUF_FIT : 5;
   // a stage is read in iterations i (K) and i + 2 (V)
   static constexpr int PREF = NBUF - 3;
   static_assert(PREF >= 2, "stages");
