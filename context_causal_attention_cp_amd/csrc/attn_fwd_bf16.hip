@@ -10,7 +10,9 @@
 //
 // One workgroup = 4 waves = 256 query rows of one segment and one head; each
 // wave owns 64 rows (two 32-row MFMA column blocks), one wave per SIMD (128
-// rows and one block per wave for calls too small to fill the chip otherwise):
+// rows and one block per wave for calls too small to fill the chip otherwise;
+// with GQA packing, 4 query heads of one KV head over 64 or 32 rows, one head
+// per wave):
 //   * K and V tiles of 32 keys are copied HBM -> LDS by range-checked buffer
 //     loads straight into LDS (no register staging), in keys-fastest layouts
 //     that need no swizzle; up to eight stages, five or six tiles in flight;
@@ -40,11 +42,12 @@
 // For qk 192 (the MLA shape) and qk 128 the main pass of 256-row workgroups runs
 // as attn_fwd_bf16_split_kernel instead: 8 waves, two per SIMD, the score waves
 // holding Q and the output waves holding O of the same 64 rows, with the
-// probabilities handed over through LDS.  A single wave per SIMD issues its
-// products, exponentials, DMA descriptors and waits in order and leaves the
-// matrix core idle whenever it stalls; with two waves per SIMD the other
-// wave's products fill those gaps.  Same arithmetic in the same order: the
-// results are bitwise those of the one-wave kernel.
+// probabilities handed over through LDS (five stages, two tiles in flight).
+// A single wave per SIMD issues its products, exponentials, DMA descriptors
+// and waits in order and leaves the matrix core idle whenever it stalls; with
+// two waves per SIMD the other wave's products fill those gaps.  Same
+// arithmetic in the same order: the results are bitwise those of the
+// one-wave kernel.
 #include <hip/hip_runtime.h>
 
 #include <climits>
