@@ -441,7 +441,7 @@ def _decode(cp, w):
     return {"shard_ms": round(ms, 4), "algorithmic_bytes_per_shard": by,
             "GB/s": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
             "TFLOP/s": round(fl / ms / 1e9, 1), "workspace_bytes": int(ws.numel()),
-            "traffic": _profiled_traffic("attn_decode_px_kernel", "attn_decode_mla.hip"),
+            "traffic": _profiled_traffic("attn_decode_rs_kernel", "attn_decode_mla.hip"),
             "merge_ms": round(mms, 4), "merge_GB/s": round(mby / mms / 1e6, 1),
             "merge_frac_hbm": round(mby / mms / 1e6 / PEAK_HBM_GBS, 4),
             "merge_cache_resident_ms": round(mms_warm, 4),
@@ -501,7 +501,7 @@ def _decode_paged(cp, w, bs):
             "paged_GB/s": round(by / paged / 1e6, 1),
             "paged_frac_hbm": round(by / paged / 1e6 / PEAK_HBM_GBS, 4),
             "paged_over_contiguous": round(paged / cont, 4),
-            "traffic_contiguous": _profiled_traffic("attn_decode_px_kernel", "attn_decode_mla.hip")}
+            "traffic_contiguous": _profiled_traffic("attn_decode_rs_kernel", "attn_decode_mla.hip")}
 
 
 def _cpu_baseline(w, q, k, v, plan, budget_s):

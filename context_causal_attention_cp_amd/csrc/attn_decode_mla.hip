@@ -13,14 +13,14 @@
 // query heads of one KV head, the partial attention over one contiguous
 // slice of the shard's keys, in tiles of 32 latent rows (36 KiB) copied
 // HBM -> LDS by buffer loads straight into LDS (no register staging):
-//   * main pass (attn_decode_px_kernel): wave w computes S^T = K Q^T for its
-//     16 heads (Q in registers, K rows read from LDS) and writes their
-//     softmax numerators P to LDS; after the tile's barrier every wave
-//     multiplies all 128 heads' P by its own 64 columns of V^T, read from the
-//     same row-major tile with the transposing ds_read_b64_tr_b16 (each
-//     latent row crosses HBM once and sits in LDS once).  Every head's
-//     softmax reference is the max of its first tile; a slice whose row sums
-//     outgrow 2^64 (or whose accumulators are not finite) is flagged;
+//   * main pass (attn_decode_rs_kernel), with split roles: waves 0-3 hold Q
+//     of 32 heads each, compute S^T = K Q^T and write the softmax numerators
+//     P to LDS; after the tile's barrier every wave multiplies all 128
+//     heads' P by its own columns of V^T, read from the same row-major tile
+//     with the transposing ds_read_b64_tr_b16 (each latent row crosses HBM
+//     once and sits in LDS once).  Every head's softmax reference is fixed
+//     at its first tile; a slice whose row sums outgrow 2^64 (or whose
+//     accumulators are not finite) is flagged;
 //   * exact pass (attn_decode_mla_kernel): recomputes only the flagged
 //     slices, each wave with 16 heads' whole 512 x 16 O^T and a reference
 //     that moves (with a rescale) when a tile outgrows it by 2^8;
@@ -49,6 +49,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -87,10 +89,9 @@ __device__ inline int swz(int key) {
   return k0 | ((k0 ^ k1) << 1) | ((k0 ^ k2) << 2);
 }
 
+// two floats -> packed bf16 (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ inline uint32_t pack_bf16(float a, float b) {
-  const __bf16 lo = (__bf16)a, hi = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // max / sum over the four 16-lane groups that hold the same head
@@ -147,10 +148,12 @@ __device__ inline void decode_item(const DecodeLaunch &D, int item, int &si, int
   row = rem / D.hkv;
 }
 
-// The exact pass: recomputes the slices the main pass (attn_decode_px_kernel)
+// The exact pass: recomputes the slices the main pass (attn_decode_rs_kernel)
 // flagged, with a per-head reference max that moves (and rescales the
 // accumulator) whenever a tile outgrows it by more than 2^8.  Each wave keeps
 // 16 heads' Q and their whole 512 x 16 O^T, so no state crosses waves.
+// Unflagged workgroups read their flag and leave (a few microseconds per
+// call; folding this pass into the main kernel made the compiler spill).
 template <bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
@@ -430,31 +433,14 @@ void attn_decode_mla_kernel(const AttnParams p, const DecodeLaunch D) {
         make_float4(oacc[b][0] * inv, oacc[b][1] * inv, oacc[b][2] * inv, oacc[b][3] * inv);
 }
 
-// ---------------------------------------------------------------------------
-// Main pass: the same slice and tiles, with the products split across the
-// waves by what each operand is shared by.  Wave w computes S^T = K Q^T for
-// its 16 heads (Q stays in its registers, K rows are read from LDS), takes
-// the softmax numerators P of those heads, and writes them to LDS; after the
-// tile's barrier every wave multiplies ALL 128 heads' P by its own 64 columns
-// of V^T (O^T[64w .. 64w + 63][all heads] lives in its accumulators).  Per
-// tile and CU that is 8 x 8 transposing reads of V^T instead of 8 x 64, and
-// 8 x 8 row reads of P: about 420 LDS read instructions instead of 800, for
-// the same 544 products.
-//   * one barrier per tile: iteration t runs PV of tile t-1 and S of tile t,
-//     so P is double-buffered (2 x 8 KiB) and four stages of 36 KiB hold the
-//     tiles being read (t-1: V, t: K) and the two in flight (t+1, t+2);
-//   * every head's softmax reference is the max of its first tile and never
-//     moves, so no wave ever rescales another wave's accumulators; a slice in
-//     which some row sum ends above 2^64 (or any accumulator is not finite) is
-//     flagged and recomputed by the exact pass (attn_decode_mla_kernel).
-// LDS of P: 16-byte units, unit (g * 128 + head) holds the eight numerators
-// of `head` that lane group g of an MFMA operand carries (keys 4g..4g+3 and
-// 16+4g..16+4g+3): the S owner writes its lane's eight at once, and a 16-lane
-// run of a reader covers 16 consecutive units (one 256-byte bank row), free of
-// bank conflicts under gfx950's lane groups for 16-byte reads.
+// Main pass (attn_decode_rs_kernel) LDS: four tile stages and two P
+// buffers.  P units are 16 bytes: unit (g * 128 + head) holds the eight
+// numerators of `head` that lane group g of an MFMA operand carries (keys
+// 4g..4g+3 and 16+4g..16+4g+3), so the S owner writes its lane's eight at
+// once, and a 16-lane run of a reader covers 16 consecutive units (one
+// 256-byte bank row), free of bank conflicts under gfx950's lane groups.
 constexpr int NBUF_X = 4;                   // main pass: LDS stages
 constexpr int PB_UNITS = 4 * HT;            // one P buffer, 16-byte units (8 KiB)
-constexpr int DBW = DV / NW / 16;           // 16-row dv blocks of O^T per wave (4)
 constexpr int HBK = HT / 16;                // 16-head blocks (8)
 constexpr float kMaxSum = 18446744073709551616.0f;  // 2^64: largest accepted row sum
 static_assert((NBUF_X * TILE_CH + 2 * PB_UNITS) * 16 <= 160 * 1024, "LDS");
@@ -480,29 +466,6 @@ __device__ inline uint32_t dma_lane_offset(int wi, int ln, int k_rs) {
 __device__ inline uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
-// 16-byte LDS read / write through inline asm (compiler-visible LDS accesses
-// in the loop would make the waitcnt pass drain the DMA queue); results are
-// consumed only after an explicit lgkmcnt wait that names them
-__device__ inline u32x4 lds_read_b128(const void *p) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-  return r;
-}
-__device__ inline void lds_write_b128(void *p, const u32x4 &v) {
-  asm volatile("ds_write_b128 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
-}
-// PV step: the eight P reads and the first V^T block's two reads complete
-// (the next block's two may still be pending); then one V^T block at a time
-__device__ inline void lds_wait_p8_v(u32x4 (&pr)[HBK], u32x2 (&v)[2]) {
-  asm volatile("s_waitcnt lgkmcnt(2)"
-               : "+v"(pr[0]), "+v"(pr[1]), "+v"(pr[2]), "+v"(pr[3]), "+v"(pr[4]), "+v"(pr[5]),
-                 "+v"(pr[6]), "+v"(pr[7]), "+v"(v[0]), "+v"(v[1]));
-}
-template <int LATER>
-__device__ inline void lds_wait_v(u32x2 (&v)[2]) {
-  if constexpr (LATER == 2) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(v[0]), "+v"(v[1]));
-  else asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]));
-}
 // vmcnt(N) and lgkmcnt(0) in one wait (gfx9 encoding)
 template <int N>
 __device__ inline void wait_vm_lgkm0() {
@@ -510,14 +473,196 @@ __device__ inline void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
+// ---------------------------------------------------------------------------
+// Main pass with split roles (attn_decode_rs_kernel).  Waves 0-3 ("score
+// waves") each hold Q of 32 heads, so every K fragment they read from LDS
+// feeds two products and the K tile is read 4 times per tile (with 16 heads
+// per wave, 8 times: 288 of ~428 KiB of LDS traffic per tile, which bound an
+// earlier P-exchange pass); waves 4-7 ("output waves") only multiply and copy.
+// The softmax numerators P go through LDS: after the tile's barrier every
+// wave multiplies all 128 heads' P by its own columns of V^T.  Score wave s
+// and output wave s + 4 share a SIMD and together own the 128 columns
+// [128 s, 128 s + 128) of O^T: the score wave 32 of them (beside its 144
+// registers of Q), the output wave 96.  The output waves copy the tiles
+// (rows 8 s'..8 s' + 7 of each tile for output wave s').  Per tile and CU:
+// 144 KiB of K reads, 8 KiB of P written and 64 KiB read, 32 KiB of V^T and
+// the 36 KiB copy, about 284 KiB.
+//   * one barrier per tile: iteration t runs S of tile t (score waves) and
+//     PV of tile t - 1 (all waves); the score waves multiply after writing
+//     P(t), the output waves after issuing the copy of tile t + 2 (both
+//     orders measured faster than the reverse); four stages and two P
+//     buffers (160 KiB); all waves at the same priority;
+//   * every head's softmax reference is the max over the first 16 keys of
+//     its first tile (the first key of the slice is always visible) and
+//     never moves; a slice whose row sums outgrow 2^64 or whose accumulators
+//     are not finite is flagged (one int32 per workgroup in the workspace)
+//     and recomputed by the exact pass (attn_decode_mla_kernel);
+//   * every LDS access in the loops is inline asm with its wait tied to the
+//     registers it fills (compiler-visible LDS reads there can make the
+//     wait-count pass drain the copies in flight).
+constexpr int RS_SDB = 2;                 // 16-column dv blocks of O^T per score wave
+constexpr int RS_ODB = 8 - RS_SDB;        // per output wave (a SIMD owns 8 blocks)
+constexpr int RS_KLA = 3;                 // K fragment reads in flight in S
+constexpr int RS_DMA = TILE_WI / 4;       // copy instructions per output wave and tile
+static_assert(TILE_WI % 4 == 0 && RS_DMA * 64 == 8 * KCH, "an output wave copies 8 rows");
+static_assert(4 * 8 * 16 == DV, "four SIMDs x 8 blocks of 16 columns");
+
+template <int OFF>
+__device__ inline u32x4 ds_read_b128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ inline u32x2 ds_read_tr16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ inline void ds_write_b128_at(uint32_t addr, const u32x4 &v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+// x is complete once at most LATER LDS operations issued after it are pending
+// (LDS operations complete in issue order)
+template <int LATER, typename T>
+__device__ inline void lgkm_tie(T &x) {
+  static_assert(LATER >= 0 && LATER < 16, "lgkmcnt");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(LATER));
+}
+template <int LATER>
+__device__ inline void lgkm_tie2(u32x2 (&v)[2]) {
+  static_assert(LATER >= 0 && LATER < 16, "lgkmcnt");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v[0]), "+v"(v[1]) : "i"(LATER));
+}
+__device__ inline void lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// K fragment of S step U: key block U / QS, k-step U % QS (two per-lane bases
+// for even and odd k-steps, as lds_bases builds them)
+template <int U>
+__device__ inline bf16x8 rs_kread(uint32_t kb0, uint32_t kb1) {
+  constexpr int MB = U / QS, ST = U % QS;
+  constexpr int OFF = 16 * KCH * 16 * MB + 128 * (ST >> 1);
+  return __builtin_bit_cast(bf16x8, ds_read_b128_at<OFF>((ST & 1) ? kb1 : kb0));
+}
+template <int U>
+__device__ inline void rs_kfirst(uint32_t kb0, uint32_t kb1, bf16x8 (&kf)[RS_KLA]) {
+  if constexpr (U < RS_KLA) {
+    kf[U] = rs_kread<U>(kb0, kb1);
+    rs_kfirst<U + 1>(kb0, kb1, kf);
+  }
+}
+// S^T = K Q^T of one tile for the score wave's two head blocks, step U
+// onwards (key block 0's 18 steps, then key block 1's); mid() runs after key
+// block 0's last products
+template <int U, typename F>
+__device__ inline void rs_qk(uint32_t kb0, uint32_t kb1, bf16x8 (&kf)[RS_KLA],
+                             const bf16x8 (&qf)[2][QS], f32x4 (&sc)[2][2], F &&mid) {
+  if constexpr (U < 2 * QS) {
+    constexpr int MB = U / QS, ST = U % QS;
+    constexpr int LATER = (2 * QS - 1 - U) < (RS_KLA - 1) ? (2 * QS - 1 - U) : (RS_KLA - 1);
+    lgkm_tie<LATER>(kf[U % RS_KLA]);
+    const bf16x8 a = kf[U % RS_KLA];
+    if constexpr (U + RS_KLA < 2 * QS) kf[U % RS_KLA] = rs_kread<U + RS_KLA>(kb0, kb1);
+    sc[MB][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ST], sc[MB][0], 0, 0, 0);
+    sc[MB][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ST], sc[MB][1], 0, 0, 0);
+    if constexpr (U == QS - 1) mid();
+    rs_qk<U + 1>(kb0, kb1, kf, qf, sc, mid);
+  }
+}
+
+// V^T fragment of this SIMD's dv block B (0..7) for keys 4g.. and 16 + 4g..
+// (ta: the stage's address plus the SIMD's 256 bytes; trb: lds_bases)
+template <int B>
+__device__ inline void rs_vread(uint32_t ta, const int (&trb)[4], u32x2 (&v)[2]) {
+  constexpr int OFF = 128 * (B >> 2);
+  v[0] = ds_read_tr16_at<OFF>(ta + trb[B & 3]);
+  v[1] = ds_read_tr16_at<OFF + 16 * KCH * 16>(ta + trb[B & 3]);
+}
+__device__ inline bf16x8 rs_vfrag(const u32x2 (&v)[2]) {
+  const u32x4 av = {v[0][0], v[0][1], v[1][0], v[1][1]};
+  return __builtin_bit_cast(bf16x8, av);
+}
+
+// Score wave's PV: its two dv blocks (both read first), P streamed one head
+// block at a time, three reads ahead (registers: Q and S are its bulk)
+template <int HB>
+__device__ inline void rs_pv_score_step(uint32_t pa, u32x4 (&pr)[3], const bf16x8 (&va)[2],
+                                        f32x4 (&oacc)[HBK][RS_SDB]) {
+  if constexpr (HB < HBK) {
+    constexpr int LATER = (HBK - 1 - HB) < 2 ? (HBK - 1 - HB) : 2;
+    lgkm_tie<LATER>(pr[HB % 3]);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, pr[HB % 3]);
+    if constexpr (HB + 3 < HBK) pr[HB % 3] = ds_read_b128_at<256 * (HB + 3)>(pa);
+    oacc[HB][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0], b, oacc[HB][0], 0, 0, 0);
+    oacc[HB][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1], b, oacc[HB][1], 0, 0, 0);
+    rs_pv_score_step<HB + 1>(pa, pr, va, oacc);
+  }
+}
+__device__ inline void rs_pv_score(uint32_t ta, uint32_t pa, const int (&trb)[4],
+                                   f32x4 (&oacc)[HBK][RS_SDB]) {
+  u32x2 v0[2], v1[2];
+  rs_vread<0>(ta, trb, v0);
+  rs_vread<1>(ta, trb, v1);
+  u32x4 pr[3];
+  pr[0] = ds_read_b128_at<0>(pa);
+  pr[1] = ds_read_b128_at<256>(pa);
+  pr[2] = ds_read_b128_at<512>(pa);
+  lgkm_tie2<3>(v0);
+  lgkm_tie2<3>(v1);
+  const bf16x8 va[2] = {rs_vfrag(v0), rs_vfrag(v1)};
+  rs_pv_score_step<0>(pa, pr, va, oacc);
+}
+
+// Output wave's PV: all eight P reads first, then its six dv blocks (2..7)
+// stream one block ahead of their eight products each
+template <int J>
+__device__ inline void rs_pv_out_step(uint32_t ta, const int (&trb)[4], const u32x4 (&pr)[HBK],
+                                      u32x2 (&vr)[2][2], f32x4 (&oacc)[HBK][RS_ODB]) {
+  if constexpr (J < RS_ODB) {
+    u32x2 (&cur)[2] = vr[J & 1];
+    if constexpr (J + 1 < RS_ODB) {
+      lgkm_tie2<2>(cur);
+    } else {
+      lgkm_tie2<0>(cur);
+    }
+    const bf16x8 a = rs_vfrag(cur);
+#pragma unroll
+    for (int hb = 0; hb < HBK; ++hb)
+      oacc[hb][J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pr[hb]),
+                                                            oacc[hb][J], 0, 0, 0);
+    if constexpr (J + 2 < RS_ODB) rs_vread<RS_SDB + J + 2>(ta, trb, cur);
+    rs_pv_out_step<J + 1>(ta, trb, pr, vr, oacc);
+  }
+}
+__device__ inline void rs_pv_out(uint32_t ta, uint32_t pa, const int (&trb)[4],
+                                 f32x4 (&oacc)[HBK][RS_ODB]) {
+  u32x4 pr[HBK];
+#pragma unroll
+  for (int hb = 0; hb < HBK; ++hb) pr[hb] = ds_read_b128_at<0>(pa + 256 * hb);
+  u32x2 vr[2][2];
+  rs_vread<RS_SDB>(ta, trb, vr[0]);
+  rs_vread<RS_SDB + 1>(ta, trb, vr[1]);
+  // the P reads and block 0's two are complete (block 1's two may pend)
+  asm volatile("s_waitcnt lgkmcnt(2)"
+               : "+v"(pr[0]), "+v"(pr[1]), "+v"(pr[2]), "+v"(pr[3]), "+v"(pr[4]), "+v"(pr[5]),
+                 "+v"(pr[6]), "+v"(pr[7]), "+v"(vr[0][0]), "+v"(vr[0][1]));
+  rs_pv_out_step<0>(ta, trb, pr, vr, oacc);
+}
+
 template <bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
-void attn_decode_px_kernel(const AttnParams p, const DecodeLaunch D) {
+void attn_decode_rs_kernel(const AttnParams p, const DecodeLaunch D) {
   __shared__ __attribute__((aligned(1024))) u32x4 lds[NBUF_X * TILE_CH + 2 * PB_UNITS];
   char *const pbuf = (char *)(lds + NBUF_X * TILE_CH);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const bool score = w < 4;
+  const int s = w & 3;  // the SIMD: heads 32 s.. (score), columns 128 s.. (both)
   const int lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int item = blockIdx.x / D.nsplit, split = blockIdx.x % D.nsplit;
   if (item >= D.items) return;
@@ -525,9 +670,6 @@ void attn_decode_px_kernel(const AttnParams p, const DecodeLaunch D) {
   decode_item(D, item, si, row, kvh, ht);
   const SegDesc sd = D.s[si];
   const int G = p.hq / p.hkv;
-  const int hl = ht * HT + w * HW + n;           // this lane's S head within the KV group
-  const bool hvalid = hl < G;
-  const int h = kvh * G + hl;
   const int64_t qrow = (int64_t)sd.q_begin + row;
   const int qpos = sd.pos_begin + row * sd.pos_stride;
 
@@ -550,260 +692,262 @@ void attn_decode_px_kernel(const AttnParams p, const DecodeLaunch D) {
   }
   const int ntiles = (k_vis - k_lo + BN - 1) / BN;
 
-  // Q fragments: B operand of S^T = K Q^T (n = head, k = d: 8 per lane group)
-  bf16x8 qf[QS];
-  {
-    const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)h * p.q_hs + 8 * g;
-#pragma unroll
-    for (int st = 0; st < QS; ++st) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (hvalid && ntiles > 0) x = *(const u32x4 *)(qp + 32 * st);
-      qf[st] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  // LDS DMA: waves 0-3 issue 5 and waves 4-7 issue 4 of the 36 instructions
-  // of a tile, through a buffer resource that ends at the slice end (rows
-  // past k_hi read as zeros)
-  const __bf16 *kbase = (const __bf16 *)p.k + (int64_t)sd.kv_begin * p.k_rs + (int64_t)kvh * p.k_hs;
-  const int wi0 = w < 4 ? 5 * w : 20 + 4 * (w - 4);
-  const int wn = w < 4 ? 5 : 4;
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)kbase, (short)0, (int)((int64_t)k_hi * p.k_rs * 2), 0x00020000);
-  const int x_lo = sd.kv_begin + k_lo;  // paged: first logical row of the slice
-  // paged: the pool block of tile t (its 32 rows sit in one block; clamped
-  // into the pool).  Looked up ahead of the DMA issue: the scalar load's
-  // wait would otherwise also wait for every LDS operation in flight.
-  auto tile_block = [&](int t) -> int {
-    if (!PAGED) return 0;
-    const int x0 = x_lo + t * BN;
-    const int b = p.block_table[(int64_t)sd.req * p.bt_stride + x0 / p.block_size];
-    return __builtin_amdgcn_readfirstlane(min(max(b, 0), p.pool_blocks - 1));
+  const uint32_t lds0 = lds_addr(lds);
+  auto stage_addr = [&](int t) -> uint32_t {
+    return lds0 + (uint32_t)((t % NBUF_X) * TILE_CH * 16);
   };
-  auto tile_rsrc = [&](int t, int b, uint32_t &row0) -> __amdgpu_buffer_rsrc_t {
-    if (!PAGED) {
-      row0 = (uint32_t)((k_lo + t * BN) * p.k_rs) * 2u;
-      return krsrc;
-    }
-    const int x0 = x_lo + t * BN;
-    const int64_t prow = (int64_t)b * p.block_size + x0 % p.block_size;
-    const int rows = min(BN, k_hi - (k_lo + t * BN));
-    row0 = 0u;
-    return __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const __bf16 *)p.k + prow * p.k_rs + (int64_t)kvh * p.k_hs), (short)0,
-        (int)(rows * p.k_rs * 2), 0x00020000);
+  // P unit of this lane as a reader (head block 0; +256 bytes per block)
+  auto p_read_addr = [&](int u) -> uint32_t {
+    const int ln = opaque_lane(lane);
+    return lds_addr(pbuf) + (uint32_t)((u & 1) * PB_UNITS * 16) +
+           (uint32_t)((((ln >> 4) * HT) + (ln & 15)) * 16);
   };
-  // per-lane DMA byte offsets: the four every wave issues are kept; the fifth
-  // (waves 0-3 only) is rebuilt at each issue from an opaque copy of the lane
-  // id -- kept live it was the register the allocator spilled, and reloading
-  // it made the compiler wait for every DMA in flight (vmcnt(0)) each tile
-  uint32_t dma_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dma_off[i] = dma_lane_offset(wi0 + i, lane, (int)p.k_rs);
-  auto issue = [&](int t, int b) {
-    uint32_t row0;
-    const __amdgpu_buffer_rsrc_t trsrc = tile_rsrc(t, b, row0);
-    u32x4 *dst = lds + (t % NBUF_X) * TILE_CH;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          trsrc, (__attribute__((address_space(3))) void *)(dst + (wi0 + i) * 64), 16,
-          row0 + dma_off[i], 0, 0, 0);
-    if (wn == 5) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          trsrc, (__attribute__((address_space(3))) void *)(dst + (wi0 + 4) * 64), 16,
-          row0 + dma_lane_offset(wi0 + 4, opaque_lane(lane), (int)p.k_rs), 0, 0, 0);
-    }
-  };
-
-  // O^T[64w + 16db + 4g + i][16hb + n] in oacc[hb][db][i]
-  f32x4 oacc[HBK][DBW];
-#pragma unroll
-  for (int hb = 0; hb < HBK; ++hb)
-#pragma unroll
-    for (int db = 0; db < DBW; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[hb][db][i] = 0.f;
-  float m_ref = 0.f;   // reference max of this lane's S head (log2 units), fixed at tile 0
-  float l_run = 0.f;   // this lane's partial row sum
-  const float sl2 = p.scale_log2;
-
-  constexpr int kRow16 = 16 * KCH * 16;
-  auto lds_bases = [&](int (&qk_base)[2], int (&tr_base)[4]) {
+  auto tr_bases = [&](int (&trb)[4]) {
     const int ln = opaque_lane(lane);
     const int nn = ln & 15, gg = ln >> 4;
-#pragma unroll
-    for (int odd = 0; odd < 2; ++odd) qk_base[odd] = 16 * (nn * KCH + ((4 * odd + gg) ^ swz(nn)));
     const int key = 4 * gg + (nn >> 2);
 #pragma unroll
     for (int b4 = 0; b4 < 4; ++b4)
-      tr_base[b4] = 16 * (key * KCH + ((2 * b4 + ((nn & 3) >> 1)) ^ swz(key))) + 8 * (nn & 1);
-  };
-  // P units of this lane (rebuilt where used from an opaque copy of the lane
-  // id, like the tile bases, instead of being kept live across the loop):
-  // the reader's unit for head block 0 (+ 256 bytes per block), the S owner's
-  auto p_units = [&](int &rd, int &wr) {
-    const int ln = opaque_lane(lane);
-    rd = ((ln >> 4) * HT + (ln & 15)) * 16;
-    wr = rd + w * HW * 16;
+      trb[b4] = 16 * (key * KCH + ((2 * b4 + ((nn & 3) >> 1)) ^ swz(key))) + 8 * (nn & 1);
   };
 
-  // O^T += V^T P^T of tile u: this wave's 64 dv columns, all 128 heads.  All
-  // eight P reads go out at once (one LDS latency for the step), then the
-  // V^T fragments stream one dv block ahead of its eight products.
-  auto pv = [&](int u) {
-    const char *tile = (const char *)(lds + (u % NBUF_X) * TILE_CH);
-    int p_rd, p_wr;
-    p_units(p_rd, p_wr);
-    const char *pb = pbuf + (u & 1) * PB_UNITS * 16 + p_rd;
-    int qk_base[2], tr_base[4];
-    lds_bases(qk_base, tr_base);
-    u32x4 pr[HBK];
-#pragma unroll
-    for (int hb = 0; hb < HBK; ++hb) pr[hb] = lds_read_b128(pb + 256 * hb);
-    u32x2 vr[2][2];
-    auto vread = [&](int db, u32x2 (&r)[2]) {
-      r[0] = lds_read_tr16(tile + tr_base[db] + 128 * w);
-      r[1] = lds_read_tr16(tile + tr_base[db] + kRow16 + 128 * w);
-    };
-    vread(0, vr[0]);
-    vread(1, vr[1]);
-    lds_wait_p8_v(pr, vr[0]);     // the P reads and V of block 0 (block 1's two may pend)
-#pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      u32x2 (&cur)[2] = vr[db & 1];
-      if (db > 0) {
-        if (db + 1 < DBW) lds_wait_v<2>(cur);
-        else lds_wait_v<0>(cur);
-      }
-      const u32x4 av = {cur[0][0], cur[0][1], cur[1][0], cur[1][1]};
-      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-      for (int hb = 0; hb < HBK; ++hb)
-        oacc[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pr[hb]),
-                                                               oacc[hb][db], 0, 0, 0);
-      if (db + 2 < DBW) vread(db + 2, cur);
-    }
-  };
-
-  if (ntiles > 0) issue(0, tile_block(0));
-  if (ntiles > 1) issue(1, tile_block(1));
-  for (int t = 0; t < ntiles; ++t) {
-    const int bnext = t + 2 < ntiles ? tile_block(t + 2) : 0;
-    // tile t has landed (only tile t + 1 may still be in flight) and this
-    // wave's P(t - 1) is written; after the barrier every wave has both
-    if (t + 1 < ntiles) {
-      if (w < 4) wait_vm_lgkm0<5>(); else wait_vm_lgkm0<4>();
-    } else {
-      wait_vm_lgkm0<0>();
-    }
-    if (PAGED) asm volatile("" : : "s"(bnext));  // the block id is in by now
-    __builtin_amdgcn_s_barrier();
-    if (t > 0) pv(t - 1);
-    // tile t + 2 goes to the stage of tile t - 2, free since the barrier;
-    // issued after the PV step rather than before it: 8 % faster
-    if (t + 2 < ntiles) issue(t + 2, bnext);
-    // ---- S^T = K Q^T of tile t for this wave's heads, their numerators
-    // against the fixed reference, written to P buffer t & 1
-    // a scheduling region of its own: the products of the PV step above
-    // would otherwise take the first slots of the pattern below
-    __builtin_amdgcn_sched_barrier(0);
-    const char *tile = (const char *)(lds + (t % NBUF_X) * TILE_CH);
-    const int j0 = k_lo + t * BN;
-    int qk_base[2], tr_base[4];
-    lds_bases(qk_base, tr_base);
-    // ---- S^T = K Q^T : two 16-key blocks x 16 heads
-    // the two key blocks' accumulation chains alternate, so consecutive
-    // products never depend on each other
-    f32x4 sc[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[mb][i] = 0.f;
-#pragma unroll
-    for (int st = 0; st < QS; ++st)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a =
-            *(const bf16x8 *)(tile + qk_base[st & 1] + kRow16 * mb + 128 * (st >> 1));
-        sc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], sc[mb], 0, 0, 0);
-      }
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads ahead
-#pragma unroll
-    for (int i = 0; i < 2 * QS - 3; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-    // ---- mask (keys at or past k_vis), numerators against the fixed reference
-    const bool full = j0 + BN <= k_vis;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float u = sc[mb][i] * sl2;
-        if (!full) u = (j0 + 16 * mb + 4 * g + i < k_vis) ? u : -INFINITY;
-        sc[mb][i] = u;
-        mx = fmaxf(mx, u);
-      }
-    if (t == 0) m_ref = max_groups(mx);   // tile 0 holds a visible key of every head
-    u32x4 pk;
-    float ls = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[mb][0] - m_ref), p1 = __builtin_amdgcn_exp2f(sc[mb][1] - m_ref);
-      const float p2 = __builtin_amdgcn_exp2f(sc[mb][2] - m_ref), p3 = __builtin_amdgcn_exp2f(sc[mb][3] - m_ref);
-      ls += (p0 + p1) + (p2 + p3);
-      pk[2 * mb] = pack_bf16(p0, p1);
-      pk[2 * mb + 1] = pack_bf16(p2, p3);
-    }
-    l_run += ls;
-    int p_rd, p_wr;
-    p_units(p_rd, p_wr);
-    lds_write_b128(pbuf + (t & 1) * PB_UNITS * 16 + p_wr, pk);
-  }
-  if (ntiles > 0) {
-    wait_vm_lgkm0<0>();             // P of the last tile written
-    __builtin_amdgcn_s_barrier();
-    pv(ntiles - 1);
-  }
-
-  // ---- flags: a row sum above 2^64 (some numerator may have left the
-  // range the fixed reference keeps exact) or a non-finite accumulator
-  const float l_tot = sum_groups(l_run);
-  bool bad = !(l_tot <= kMaxSum);
-#pragma unroll
-  for (int hb = 0; hb < HBK; ++hb)
-#pragma unroll
-    for (int db = 0; db < DBW; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bad = bad || !__builtin_isfinite(oacc[hb][db][i]);
-  const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-  // row sums of all heads and the waves' flags through the P buffer that no
-  // wave reads any more (the last tile's P is in the other one)
-  float *xch = (float *)(pbuf + (ntiles & 1) * PB_UNITS * 16);
-  if (g == 0) xch[w * HW + n] = l_tot;
-  if (lane == 0) ((int *)xch)[HT + w] = wave_bad ? 1 : 0;
-  __syncthreads();
-  int flagged = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) flagged |= ((const int *)xch)[HT + i];
-  if (tid == 0) D.ws_flags[blockIdx.x] = flagged;
-  if (flagged) return;  // the exact pass writes this slice
+  float l_tot[2] = {0.f, 0.f};  // score waves: row sums of the lane's two heads
+  float m_ref[2] = {0.f, 0.f};  // and their references (log2 units)
+  bool bad = false;
   const int64_t part = (int64_t)item * D.nsplit + split;
-  if (g == 0 && hvalid)
-    D.ws_lse[part * HT + w * HW + n] =
-        l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+  int flagged = 0;
+
+  if (score) {
+    // ---- score wave: S, the numerators of heads 32 s + 16 hb + n, PV of
+    // columns [128 s, 128 s + 32)
+    bf16x8 qf[2][QS];
 #pragma unroll
-  for (int hb = 0; hb < HBK; ++hb) {
-    const float lt = xch[16 * hb + n];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float *wo = D.ws_o + (part * HT + 16 * hb + n) * DV + 64 * w + 4 * g;
+    for (int hb = 0; hb < 2; ++hb) {
+      const int hl = ht * HT + 32 * s + 16 * hb + n;
+      const bool hvalid = hl < G;
+      const __bf16 *qp = (const __bf16 *)p.q + qrow * p.q_rs + (int64_t)(kvh * G + hl) * p.q_hs + 8 * g;
 #pragma unroll
-    for (int db = 0; db < DBW; ++db)
-      *(float4 *)(wo + 16 * db) = make_float4(oacc[hb][db][0] * inv, oacc[hb][db][1] * inv,
-                                              oacc[hb][db][2] * inv, oacc[hb][db][3] * inv);
+      for (int st = 0; st < QS; ++st) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (hvalid && ntiles > 0) x = *(const u32x4 *)(qp + 32 * st);
+        qf[hb][st] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+    f32x4 oacc[HBK][RS_SDB];
+#pragma unroll
+    for (int hb = 0; hb < HBK; ++hb)
+#pragma unroll
+      for (int j = 0; j < RS_SDB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[hb][j][i] = 0.f;
+    float l_run[2] = {0.f, 0.f};
+    const float sl2 = p.scale_log2;
+    auto pv = [&](int u) {
+      int trb[4];
+      tr_bases(trb);
+      rs_pv_score(stage_addr(u) + 256u * (uint32_t)s, p_read_addr(u), trb, oacc);
+    };
+    for (int t = 0; t < ntiles; ++t) {
+      lgkm0();  // this wave's P(t - 1) is written
+      __builtin_amdgcn_s_barrier();
+      const int j0 = k_lo + t * BN;
+      const bool full = j0 + BN <= k_vis;
+      // K row bases of this lane for even and odd k-steps
+      uint32_t kb0, kb1;
+      {
+        const int ln = opaque_lane(lane);
+        const int nn = ln & 15, gg = ln >> 4;
+        const uint32_t ta = stage_addr(t);
+        kb0 = ta + (uint32_t)(16 * (nn * KCH + (gg ^ swz(nn))));
+        kb1 = ta + (uint32_t)(16 * (nn * KCH + ((4 + gg) ^ swz(nn))));
+      }
+      f32x4 sc[2][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[mb][hb][i] = 0.f;
+      u32x4 pk[2];
+      // numerators of key block mb against the fixed references: P-unit
+      // elements 4 mb .. 4 mb + 3 (keys 16 mb + 4g + i)
+      auto numer = [&](int mb) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          float u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u[i] = sc[mb][hb][i] * sl2;
+            if (!full) u[i] = (j0 + 16 * mb + 4 * g + i < k_vis) ? u[i] : -INFINITY;
+          }
+          if (mb == 0 && t == 0)  // the slice's first key is visible
+            m_ref[hb] = max_groups(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])));
+          const float p0 = __builtin_amdgcn_exp2f(u[0] - m_ref[hb]);
+          const float p1 = __builtin_amdgcn_exp2f(u[1] - m_ref[hb]);
+          const float p2 = __builtin_amdgcn_exp2f(u[2] - m_ref[hb]);
+          const float p3 = __builtin_amdgcn_exp2f(u[3] - m_ref[hb]);
+          l_run[hb] += (p0 + p1) + (p2 + p3);
+          pk[hb][2 * mb] = pack_bf16(p0, p1);
+          pk[hb][2 * mb + 1] = pack_bf16(p2, p3);
+        }
+      };
+      bf16x8 kf[RS_KLA];
+      rs_kfirst<0>(kb0, kb1, kf);
+      rs_qk<0>(kb0, kb1, kf, qf, sc, [&]() { numer(0); });
+      numer(1);
+      {
+        const int ln = opaque_lane(lane);
+        const uint32_t pw = lds_addr(pbuf) + (uint32_t)((t & 1) * PB_UNITS * 16) +
+                            (uint32_t)((((ln >> 4) * HT) + 32 * s + (ln & 15)) * 16);
+        ds_write_b128_at<0>(pw, pk[0]);
+        ds_write_b128_at<256>(pw, pk[1]);
+      }
+      if (t > 0) pv(t - 1);
+    }
+    if (ntiles > 0) {
+      lgkm0();
+      __builtin_amdgcn_s_barrier();
+      pv(ntiles - 1);
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      l_tot[hb] = sum_groups(l_run[hb]);
+      bad = bad || !(l_tot[hb] <= kMaxSum);
+    }
+#pragma unroll
+    for (int hb = 0; hb < HBK; ++hb)
+#pragma unroll
+      for (int j = 0; j < RS_SDB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad = bad || !__builtin_isfinite(oacc[hb][j][i]);
+    // ---- epilogue below, after the flags are exchanged
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    float *xch = (float *)(pbuf + (ntiles & 1) * PB_UNITS * 16);
+    if (g == 0) {
+      xch[32 * s + n] = l_tot[0];
+      xch[32 * s + 16 + n] = l_tot[1];
+    }
+    if (lane == 0) ((int *)xch)[HT + w] = wave_bad ? 1 : 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) flagged |= ((const int *)xch)[HT + i];
+    if (!flagged) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int hl = ht * HT + 32 * s + 16 * hb + n;
+      if (g == 0 && hl < G)
+        D.ws_lse[part * HT + 32 * s + 16 * hb + n] =
+            l_tot[hb] > 0.f ? (m_ref[hb] + log2f(l_tot[hb])) * kLn2 : -INFINITY;
+    }
+#pragma unroll
+    for (int hb = 0; hb < HBK; ++hb) {
+      const float lt = xch[16 * hb + n];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float *wo = D.ws_o + (part * HT + 16 * hb + n) * DV + 128 * s + 4 * g;
+#pragma unroll
+      for (int j = 0; j < RS_SDB; ++j)
+        *(float4 *)(wo + 16 * j) = make_float4(oacc[hb][j][0] * inv, oacc[hb][j][1] * inv,
+                                               oacc[hb][j][2] * inv, oacc[hb][j][3] * inv);
+    }
+    }
+  } else {
+    // ---- output wave: copies rows 8 s .. 8 s + 7 of each tile, PV of
+    // columns [128 s + 32, 128 s + 128)
+    const __bf16 *kbase =
+        (const __bf16 *)p.k + (int64_t)sd.kv_begin * p.k_rs + (int64_t)kvh * p.k_hs;
+    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)kbase, (short)0, (int)((int64_t)k_hi * p.k_rs * 2), 0x00020000);
+    const int x_lo = sd.kv_begin + k_lo;
+    auto tile_block = [&](int t) -> int {
+      if (!PAGED) return 0;
+      const int x0 = x_lo + t * BN;
+      const int b = p.block_table[(int64_t)sd.req * p.bt_stride + x0 / p.block_size];
+      return __builtin_amdgcn_readfirstlane(min(max(b, 0), p.pool_blocks - 1));
+    };
+    auto tile_rsrc = [&](int t, int b, uint32_t &row0) -> __amdgpu_buffer_rsrc_t {
+      if (!PAGED) {
+        row0 = (uint32_t)((k_lo + t * BN) * p.k_rs) * 2u;
+        return krsrc;
+      }
+      const int x0 = x_lo + t * BN;
+      const int64_t prow = (int64_t)b * p.block_size + x0 % p.block_size;
+      const int rows = min(BN, k_hi - (k_lo + t * BN));
+      row0 = 0u;
+      return __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((const __bf16 *)p.k + prow * p.k_rs + (int64_t)kvh * p.k_hs), (short)0,
+          (int)(rows * p.k_rs * 2), 0x00020000);
+    };
+    // per-lane copy offsets: four kept, the other five rebuilt at each issue
+    uint32_t dma_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_off[i] = dma_lane_offset(RS_DMA * s + i, lane, (int)p.k_rs);
+    auto issue = [&](int t, int b) {
+      uint32_t row0;
+      const __amdgpu_buffer_rsrc_t trsrc = tile_rsrc(t, b, row0);
+      u32x4 *dst = lds + (t % NBUF_X) * TILE_CH + RS_DMA * s * 64;
+#pragma unroll
+      for (int i = 0; i < RS_DMA; ++i) {
+        const uint32_t off =
+            i < 4 ? dma_off[i] : dma_lane_offset(RS_DMA * s + i, opaque_lane(lane), (int)p.k_rs);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            trsrc, (__attribute__((address_space(3))) void *)(dst + i * 64), 16, row0 + off, 0, 0,
+            0);
+      }
+    };
+    f32x4 oacc[HBK][RS_ODB];
+#pragma unroll
+    for (int hb = 0; hb < HBK; ++hb)
+#pragma unroll
+      for (int j = 0; j < RS_ODB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[hb][j][i] = 0.f;
+    auto pv = [&](int u) {
+      int trb[4];
+      tr_bases(trb);
+      rs_pv_out(stage_addr(u) + 256u * (uint32_t)s, p_read_addr(u), trb, oacc);
+    };
+    if (ntiles > 0) issue(0, tile_block(0));
+    if (ntiles > 1) issue(1, tile_block(1));
+    for (int t = 0; t < ntiles; ++t) {
+      const int bnext = t + 2 < ntiles ? tile_block(t + 2) : 0;
+      // this wave's rows of tile t have landed (tile t + 1's may pend)
+      if (t + 1 < ntiles) wait_vm_lgkm0<RS_DMA>(); else wait_vm_lgkm0<0>();
+      if (PAGED) asm volatile("" : : "s"(bnext));
+      __builtin_amdgcn_s_barrier();
+      // tile t + 2 goes to the stage of tile t - 2, free since the barrier
+      if (t + 2 < ntiles) issue(t + 2, bnext);
+      if (t > 0) pv(t - 1);
+    }
+    if (ntiles > 0) {
+      wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      pv(ntiles - 1);
+    }
+#pragma unroll
+    for (int hb = 0; hb < HBK; ++hb)
+#pragma unroll
+      for (int j = 0; j < RS_ODB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad = bad || !__builtin_isfinite(oacc[hb][j][i]);
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    float *xch = (float *)(pbuf + (ntiles & 1) * PB_UNITS * 16);
+    if (lane == 0) ((int *)xch)[HT + w] = wave_bad ? 1 : 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) flagged |= ((const int *)xch)[HT + i];
+    if (tid == 256) D.ws_flags[blockIdx.x] = flagged;
+    if (!flagged) {
+#pragma unroll
+    for (int hb = 0; hb < HBK; ++hb) {
+      const float lt = xch[16 * hb + n];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float *wo = D.ws_o + (part * HT + 16 * hb + n) * DV + 128 * s + 16 * RS_SDB + 4 * g;
+#pragma unroll
+      for (int j = 0; j < RS_ODB; ++j)
+        *(float4 *)(wo + 16 * j) = make_float4(oacc[hb][j][0] * inv, oacc[hb][j][1] * inv,
+                                               oacc[hb][j][2] * inv, oacc[hb][j][3] * inv);
+    }
+    }
   }
 }
 
@@ -824,20 +968,45 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const AttnPara
   const int h = kvh * G + hl;
   const int64_t qrow = (int64_t)sd.q_begin + row;
   const int64_t part0 = (int64_t)item * D.nsplit;
+  const int ns = D.nsplit;
+  // the first CMB_PRE slices' log-sum-exps and partial rows are loaded at
+  // once, before any of them is used (every slice's partial is written, by
+  // the main or the exact pass), so the wave waits for memory once
+  constexpr int CMB_PRE = 4;
+  float lsv[CMB_PRE];
+  float4 xa[CMB_PRE], xb[CMB_PRE];
+#pragma unroll
+  for (int s = 0; s < CMB_PRE; ++s) {
+    lsv[s] = -INFINITY;
+    xa[s] = xb[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s < ns) {
+      lsv[s] = D.ws_lse[(part0 + s) * HT + hloc];
+      const float *src = D.ws_o + ((part0 + s) * HT + hloc) * DV + lane * 8;
+      xa[s] = *(const float4 *)src;
+      xb[s] = *(const float4 *)(src + 4);
+    }
+  }
   float m = -INFINITY;
-  for (int s = 0; s < D.nsplit; ++s) m = fmaxf(m, D.ws_lse[(part0 + s) * HT + hloc]);
+#pragma unroll
+  for (int s = 0; s < CMB_PRE; ++s) m = fmaxf(m, lsv[s]);
+  for (int s = CMB_PRE; s < ns; ++s) m = fmaxf(m, D.ws_lse[(part0 + s) * HT + hloc]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
+  auto add = [&](float ls, const float4 &a, const float4 &b) {
+    const float wgt = expf(ls - m);
+    wsum += wgt;
+    acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
+    acc[4] += wgt * b.x; acc[5] += wgt * b.y; acc[6] += wgt * b.z; acc[7] += wgt * b.w;
+  };
   if (m != -INFINITY) {
-    for (int s = 0; s < D.nsplit; ++s) {
+#pragma unroll
+    for (int s = 0; s < CMB_PRE; ++s)
+      if (lsv[s] != -INFINITY) add(lsv[s], xa[s], xb[s]);
+    for (int s = CMB_PRE; s < ns; ++s) {
       const float ls = D.ws_lse[(part0 + s) * HT + hloc];
       if (ls == -INFINITY) continue;
-      const float wgt = expf(ls - m);
-      wsum += wgt;
       const float *src = D.ws_o + ((part0 + s) * HT + hloc) * DV + lane * 8;
-      const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
-      acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
-      acc[4] += wgt * b.x; acc[5] += wgt * b.y; acc[6] += wgt * b.z; acc[7] += wgt * b.w;
+      add(ls, *(const float4 *)src, *(const float4 *)(src + 4));
     }
   }
   float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -892,10 +1061,10 @@ hipError_t launch_attn_decode_mla(const AttnParams &p, const DecodeLaunch &D, hi
   // main pass (flags the slices it cannot keep exact), then the exact pass
   // over the flagged slices only
   if (p.block_table) {
-    hipLaunchKernelGGL(attn_decode_px_kernel<true>, grid, dim3(NT), 0, stream, p, D);
+    hipLaunchKernelGGL(attn_decode_rs_kernel<true>, grid, dim3(NT), 0, stream, p, D);
     hipLaunchKernelGGL(attn_decode_mla_kernel<true>, grid, dim3(NT), 0, stream, p, D);
   } else {
-    hipLaunchKernelGGL(attn_decode_px_kernel<false>, grid, dim3(NT), 0, stream, p, D);
+    hipLaunchKernelGGL(attn_decode_rs_kernel<false>, grid, dim3(NT), 0, stream, p, D);
     hipLaunchKernelGGL(attn_decode_mla_kernel<false>, grid, dim3(NT), 0, stream, p, D);
   }
   hipError_t e = hipGetLastError();
