@@ -774,18 +774,29 @@ void attn_decode_rs_kernel(const AttnParams p, const DecodeLaunch D) {
       auto numer = [&](int mb) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-          float u[4];
+          if (mb == 0 && t == 0) {  // the slice's first key is visible
+            float u[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            u[i] = sc[mb][hb][i] * sl2;
-            if (!full) u[i] = (j0 + 16 * mb + 4 * g + i < k_vis) ? u[i] : -INFINITY;
-          }
-          if (mb == 0 && t == 0)  // the slice's first key is visible
+            for (int i = 0; i < 4; ++i) {
+              u[i] = sc[mb][hb][i] * sl2;
+              if (!full) u[i] = (j0 + 16 * mb + 4 * g + i < k_vis) ? u[i] : -INFINITY;
+            }
             m_ref[hb] = max_groups(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])));
-          const float p0 = __builtin_amdgcn_exp2f(u[0] - m_ref[hb]);
-          const float p1 = __builtin_amdgcn_exp2f(u[1] - m_ref[hb]);
-          const float p2 = __builtin_amdgcn_exp2f(u[2] - m_ref[hb]);
-          const float p3 = __builtin_amdgcn_exp2f(u[3] - m_ref[hb]);
+          }
+          // scaled score minus the reference in one rounding
+          const float nm = -m_ref[hb];
+          float x[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = fmaf(sc[mb][hb][i], sl2, nm);
+          if (!full) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              x[i] = (j0 + 16 * mb + 4 * g + i < k_vis) ? x[i] : -INFINITY;
+          }
+          const float p0 = __builtin_amdgcn_exp2f(x[0]);
+          const float p1 = __builtin_amdgcn_exp2f(x[1]);
+          const float p2 = __builtin_amdgcn_exp2f(x[2]);
+          const float p3 = __builtin_amdgcn_exp2f(x[3]);
           l_run[hb] += (p0 + p1) + (p2 + p3);
           pk[hb][2 * mb] = pack_bf16(p0, p1);
           pk[hb][2 * mb + 1] = pack_bf16(p2, p3);

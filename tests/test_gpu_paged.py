@@ -201,3 +201,21 @@ def test_paged_gqa_empty_and_invisible():
     for b in (1, 2):
         lb = f64(l[b])
         assert np.all(lb == -np.inf) and np.all(f64(o[b]) == 0), f"req {b}: not empty"
+
+
+def test_paged_repeatable():
+    """The same paged and contiguous shard calls, repeated: every repeat is
+    bitwise equal to the first (a run-to-run difference would mean a race
+    between the waves of a workgroup)."""
+    B, ctx, W, bs, hq = 3, 1000, 4, 128, 128
+    say("paged decode repeatability")
+    q, kv = _inputs(B, ctx, hq, ctx + bs)
+    scale = 1.0 / np.sqrt(DQK)
+    q_pos = [ctx] + [ctx - 1 - 211 * b for b in range(1, B)]
+    pg = _Paged(kv, W, 0, bs, seed=0)
+    for run in (pg.run, pg.run_contiguous):
+        o0, l0 = run(q, q_pos, scale)
+        for rep in range(6):
+            o, l = run(q, q_pos, scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o0) and torch.equal(l, l0), f"{run.__name__}: repeat {rep} differs"
