@@ -747,20 +747,16 @@ void attn_decode_rs_kernel(const AttnParams p, const DecodeLaunch D) {
       tr_bases(trb);
       rs_pv_score(stage_addr(u) + 256u * (uint32_t)s, p_read_addr(u), trb, oacc);
     };
+    // K row bases of this lane for even and odd k-steps (kept across the loop)
+    const uint32_t kl0 = (uint32_t)(16 * (n * KCH + (g ^ swz(n))));
+    const uint32_t kl1 = (uint32_t)(16 * (n * KCH + ((4 + g) ^ swz(n))));
     for (int t = 0; t < ntiles; ++t) {
       lgkm0();  // this wave's P(t - 1) is written
       __builtin_amdgcn_s_barrier();
       const int j0 = k_lo + t * BN;
       const bool full = j0 + BN <= k_vis;
       // K row bases of this lane for even and odd k-steps
-      uint32_t kb0, kb1;
-      {
-        const int ln = opaque_lane(lane);
-        const int nn = ln & 15, gg = ln >> 4;
-        const uint32_t ta = stage_addr(t);
-        kb0 = ta + (uint32_t)(16 * (nn * KCH + (gg ^ swz(nn))));
-        kb1 = ta + (uint32_t)(16 * (nn * KCH + ((4 + gg) ^ swz(nn))));
-      }
+      const uint32_t kb0 = stage_addr(t) + kl0, kb1 = stage_addr(t) + kl1;
       f32x4 sc[2][2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
