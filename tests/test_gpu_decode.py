@@ -45,7 +45,10 @@ def _oracle_shard(q64, kv64, b, j, W, scale, q_pos, causal=True):
                      keys, scale, causal)
 
 
-@pytest.mark.parametrize("B,ctx,W,hq", [(3, 1000, 4, 128), (2, 777, 2, 16), (1, 4100, 1, 160)])
+# head counts that end inside a score wave's 32 heads or inside one of its
+# 16-head blocks (8, 40, 100) as well as whole ones
+@pytest.mark.parametrize("B,ctx,W,hq", [(3, 1000, 4, 128), (2, 777, 2, 16), (1, 4100, 1, 160),
+                                        (2, 600, 1, 8), (2, 900, 2, 40), (1, 1300, 3, 100)])
 def test_decode_shards_small(B, ctx, W, hq):
     say(f"decode small B={B} ctx={ctx} W={W} hq={hq}")
     g = torch.Generator(device=DEV)
