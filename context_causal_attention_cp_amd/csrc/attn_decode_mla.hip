@@ -865,10 +865,16 @@ void attn_decode_rs_kernel(const AttnParams p, const DecodeLaunch D) {
     const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)kbase, (short)0, (int)((int64_t)k_hi * p.k_rs * 2), 0x00020000);
     const int x_lo = sd.kv_begin + k_lo;
+    // (read through the constant address space: the table is not written
+    // during the kernel, so the uniform read is a scalar load, whose wait
+    // leaves the copies in flight alone; a vector load here made the
+    // compiler wait for every copy in flight, vmcnt(0), each tile)
+    const __attribute__((address_space(4))) int32_t *btab =
+        (const __attribute__((address_space(4))) int32_t *)(uintptr_t)p.block_table;
     auto tile_block = [&](int t) -> int {
       if (!PAGED) return 0;
       const int x0 = x_lo + t * BN;
-      const int b = p.block_table[(int64_t)sd.req * p.bt_stride + x0 / p.block_size];
+      const int b = btab[(int64_t)sd.req * p.bt_stride + x0 / p.block_size];
       return __builtin_amdgcn_readfirstlane(min(max(b, 0), p.pool_blocks - 1));
     };
     auto tile_rsrc = [&](int t, int b, uint32_t &row0) -> __amdgpu_buffer_rsrc_t {
