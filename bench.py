@@ -39,7 +39,7 @@ def _args():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--only", choices=["decode", "decode_paged", "restore", "zigzag_t8192_p1024",
-                                       "interleave_b12"],
+                                       "interleave_b12", "peaks"],
                     help="only this measurement of the extra section (for profiling)")
     return ap.parse_args()
 
@@ -244,10 +244,15 @@ def main():
         out["extra"]["decode_mla_b64"] = _decode(cp, workloads.get("decode_mla_b64"))
         out["extra"]["decode_mla_b64_paged_block128"] = _decode_paged(
             cp, workloads.get("decode_mla_b64"), 128)
-        mp = _measured_peaks()
+        mp = _measured_peaks(cp)
         out["measured_peaks"] = mp
+        out["roofline"]["frac_of_measured_mfma_loop"] = round(
+            out["roofline"]["achieved"] / mp["mfma_loop_TFLOP/s"], 4)
         out["roofline"]["frac_of_measured_gemm"] = round(
             out["roofline"]["achieved"] / mp["bf16_gemm_TFLOP/s"], 4)
+        out["merge"]["frac_of_measured_copy"] = round(out["merge"]["GB/s"] / mp["copy_GB/s"], 4)
+        dec = out["extra"]["decode_mla_b64"]
+        dec["frac_of_measured_copy"] = round(dec["GB/s"] / mp["copy_GB/s"], 4)
     print(json.dumps(out), flush=True)
 
 
@@ -260,6 +265,8 @@ def _only(cp, name):
         out = _prefill_ranks(cp, workloads.get(name))
     elif name == "decode_paged":
         out = _decode_paged(cp, workloads.get("decode_mla_b64"), 128)
+    elif name == "peaks":
+        out = _measured_peaks(cp)
     else:
         w = workloads.get("zigzag_t131072_mla")
         _, k, _ = workloads.prefill_tensors(w, "cuda")
@@ -287,11 +294,31 @@ def _time_cold_ms(fn, reps=10):
     return float(np.median(times))
 
 
-def _measured_peaks():
-    """A sustained rate measured on this GPU in the same run, as a reference
-    beside the published peak: a large bf16 GEMM through torch (hipBLASLt).
-    The bandwidth kernels are reported against the published 8 TB/s only."""
+def _measured_peaks(cp):
+    """Sustained rates measured on this GPU in the same run, as references
+    beside the published peaks (the fractions in "roofline", "merge" and the
+    extras stay against the published ones): the library's matrix-core loop
+    (independent bf16 32x32x16 products on register operands, at the clock
+    the chip holds under that load), its streamed device copy, and a large
+    bf16 GEMM through torch (hipBLASLt)."""
+    import numpy as np
     import torch
+    # matrix-core loop: 2 workgroups of 4 waves per compute unit
+    wgs, iters = 2 * torch.cuda.get_device_properties(0).multi_processor_count, 16384
+    out = torch.empty(wgs * 4, device="cuda", dtype=torch.float32)
+    mfma_ms = _time_ms(lambda: cp.calib_mfma(wgs, iters, out), reps=5, warm=2)
+    torch.cuda.synchronize()
+    if not bool((out == 8.0 * 16 * iters).all()):
+        raise RuntimeError("matrix-core loop returned wrong sums")
+    mfma_flops = wgs * 4 * iters * 8 * 2.0 * 32 * 32 * 16
+    # streamed copy of 4 GiB
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    copy_ms = _time_ms(lambda: cp.calib_copy(src, dst), reps=5, warm=2)
+    del src, dst
+    torch.cuda.empty_cache()
     n = 8192
     a = torch.randn((n, n), device="cuda", dtype=torch.float32).to(torch.bfloat16)
     b = torch.randn((n, n), device="cuda", dtype=torch.float32).to(torch.bfloat16)
@@ -299,7 +326,12 @@ def _measured_peaks():
     gemm_ms = _time_ms(lambda: torch.mm(a, b, out=c), reps=10, warm=3)
     del a, b, c
     torch.cuda.empty_cache()
-    return {"bf16_gemm_TFLOP/s": round(2.0 * n ** 3 / gemm_ms / 1e9, 1),
+    return {"mfma_loop_TFLOP/s": round(mfma_flops / mfma_ms / 1e9, 1),
+            "mfma_loop_what": "cp_calib_mfma: %d workgroups x 4 waves x %d rounds of 8 independent "
+                              "bf16 32x32x16 products, mean of 5" % (wgs, iters),
+            "copy_GB/s": round(2.0 * nbytes / copy_ms / 1e6, 1),
+            "copy_what": "cp_calib_copy of 4 GiB (read + write bytes), mean of 5",
+            "bf16_gemm_TFLOP/s": round(2.0 * n ** 3 / gemm_ms / 1e9, 1),
             "bf16_gemm_what": "torch.mm bf16 8192 x 8192 x 8192 (hipBLASLt), mean of 10"}
 
 

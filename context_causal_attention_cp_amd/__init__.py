@@ -8,6 +8,7 @@ gather.  This package is the thin ctypes binding over it.
 """
 from ._lib import (  # noqa: F401
     CP_BF16, CP_F32, CP_INTERLEAVE, CP_ZIGZAG, EXPORTS, LIB_PATH, PASS_KV, PASS_Q, CpError,
-    Segment, ShardPlan, attn_fwd, attn_fwd_noalloc, attn_workspace_size, choose_pass, lse_merge, restore_apply,
+    Segment, ShardPlan, attn_fwd, attn_fwd_noalloc, attn_workspace_size, calib_copy, calib_mfma, choose_pass,
+    lse_merge, restore_apply,
     restore_index, ring_pad_len, shard_plan, status_str, version,
 )

@@ -22,7 +22,8 @@ CP_F32, CP_BF16 = 0, 1
 
 EXPORTS = ("cp_shard_plan", "cp_restore_index", "cp_restore_apply", "cp_choose_pass",
            "cp_ring_pad_len", "cp_attn_workspace_size", "cp_attn_fwd", "cp_attn_fwd_noalloc",
-           "cp_lse_merge", "cp_status_str", "cp_last_error", "cp_version")
+           "cp_lse_merge", "cp_status_str", "cp_last_error", "cp_version", "cp_calib_mfma",
+           "cp_calib_copy")
 NOALLOC_SCRATCH_BYTES = 128 << 20   # CP_NOALLOC_SCRATCH_BYTES
 
 _STRATEGY = {"zigzag": CP_ZIGZAG, "interleave": CP_INTERLEAVE}
@@ -95,6 +96,10 @@ def _load():
     lib.cp_ring_pad_len.restype = i32
     lib.cp_ring_pad_len.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), i64,
                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.cp_calib_mfma.restype = i32
+    lib.cp_calib_mfma.argtypes = [i32, i32, vp, vp]
+    lib.cp_calib_copy.restype = i32
+    lib.cp_calib_copy.argtypes = [vp, vp, i64, vp]
     lib.cp_attn_workspace_size.restype = i32
     lib.cp_attn_workspace_size.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.cp_attn_fwd.restype = i32
@@ -403,6 +408,30 @@ def restore_apply(index, src, out=None, stream=None):
     if s != CP_OK:
         raise CpError(s, "cp_restore_apply")
     return out
+
+
+def calib_mfma(workgroups: int, iters: int, out, stream=None):
+    """cp_calib_mfma: the matrix-core loop; ``out`` fp32 [workgroups * 4] on
+    the device receives 8 * 16 * iters per wave."""
+    stream = _stream(stream)
+    s = _lib.cp_calib_mfma(workgroups, iters, out.data_ptr(), ctypes.c_void_p(_stream_handle(stream)))
+    if s != CP_OK:
+        raise CpError(s, "cp_calib_mfma")
+    return out
+
+
+def calib_copy(src, dst, stream=None):
+    """cp_calib_copy: dst[:] = src[:] (both contiguous device tensors of the
+    same size in bytes, a multiple of 16)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous and of the same size")
+    stream = _stream(stream)
+    s = _lib.cp_calib_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                           ctypes.c_void_p(_stream_handle(stream)))
+    if s != CP_OK:
+        raise CpError(s, "cp_calib_copy")
+    return dst
 
 
 PASS_KV, PASS_Q = 0, 1

@@ -678,6 +678,24 @@ extern "C" cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads
   return e == hipSuccess ? CP_OK : device_error(e);
 }
 
+extern "C" cp_status cp_calib_mfma(int32_t workgroups, int32_t iters, float *out, void *stream) {
+  if (workgroups < 1 || iters < 1 || !out) return CP_ERR_ARG;
+  if (iters > (1 << 17)) return CP_ERR_ARG;  // 8 * 16 * iters stays exact in fp32
+  (void)hipGetLastError();
+  const hipError_t e = launch_calib_mfma(workgroups, iters, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CP_OK : device_error(e);
+}
+
+extern "C" cp_status cp_calib_copy(const void *src, void *dst, int64_t bytes, void *stream) {
+  if (bytes < 0 || bytes % 16 != 0) return CP_ERR_ARG;
+  if (bytes == 0) return CP_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return CP_ERR_ARG;
+  if (bytes / 1024 >= INT32_MAX) return CP_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipError_t e = launch_calib_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CP_OK : device_error(e);
+}
+
 extern "C" cp_status cp_restore_apply(const int32_t *index, int64_t n, const void *src,
                                       int64_t src_rows, int64_t src_row_stride, void *dst,
                                       int64_t dst_row_stride, int64_t row_bytes, void *stream) {

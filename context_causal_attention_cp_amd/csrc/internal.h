@@ -106,6 +106,8 @@ hipError_t launch_attn_decode_mla(const AttnParams &p, const DecodeLaunch &D,
 int attn_bf16_tile_rows(int dqk, int dv, bool small);
 int attn_f32_tile_rows(int d);
 
+hipError_t launch_calib_mfma(int32_t workgroups, int32_t iters, float *out, hipStream_t stream);
+hipError_t launch_calib_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_restore_apply(const int32_t *index, int64_t n, const void *src, int64_t src_rows,
                                 int64_t src_stride, void *dst, int64_t dst_stride,
                                 int64_t row_bytes, hipStream_t stream);

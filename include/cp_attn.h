@@ -342,6 +342,28 @@ cp_status cp_lse_merge(int32_t num_parts, int32_t rows, int32_t heads,
                        int64_t lse_part_stride, void *o_out, int32_t out_dtype,
                        float *lse_out, void *stream);
 
+/*
+ * cp_calib_mfma -- sustained matrix-core rate of this GPU (a measurement
+ * aid, not part of the attention path).  Each of `workgroups` workgroups of
+ * 256 threads runs, per wave, `iters` rounds of 8 independent bf16 32x32x16
+ * products with fp32 accumulation on register operands: 2 * 32 * 32 * 16 *
+ * 8 * iters FLOPs per wave.  out: device fp32 [workgroups * 4], one value
+ * per wave, 8 * 16 * iters exactly.  Errors: CP_ERR_ARG (workgroups < 1,
+ * iters outside 1 .. 2^17, NULL out), CP_ERR_DEVICE.  Enqueued on `stream`.
+ *
+ * cp_calib_copy -- device copy dst[0, bytes) = src[0, bytes) in 16-byte
+ * units, streamed past the caches (the measured copy bandwidth of this GPU:
+ * bytes read + bytes written per second).  Both pointers device memory,
+ * 16-byte aligned, not overlapping; bytes a multiple of 16.  Errors:
+ * CP_ERR_ARG, CP_ERR_UNSUPPORTED (more than 2 TiB), CP_ERR_DEVICE.
+ *
+ * Both report what this chip reaches at the clock it holds under load, so
+ * that kernels can be stated against a measured ceiling beside the
+ * published peaks.
+ */
+cp_status cp_calib_mfma(int32_t workgroups, int32_t iters, float *out, void *stream);
+cp_status cp_calib_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *cp_status_str(int32_t status);
 
