@@ -242,6 +242,24 @@ __device__ inline void split_tr_reads(uint32_t addr, u32x2 (&vl)[OB], u32x2 (&vh
     vh[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B) + 128 * VCH>(addr)),
    ...);
 }
+// O^T += V^T P^T for 16-key step C (both row blocks) from registers; each
+// dv block's V^T registers take the same block of the next tile (the stage at
+// addr) right after their two products, so the reads run among the products
+// and no second register set is needed
+template <int VCH, int OB, int C, int... B>
+__device__ inline void reload_mma(uint32_t addr, u32x2 (&vl)[OB], u32x2 (&vh)[OB],
+                                  const bf16x8 (&pf)[2], f32x16 (&oacc)[OB][2],
+                                  std::integer_sequence<int, B...>) {
+  ((oacc[B][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, (u32x4){vl[B][0], vl[B][1], vh[B][0], vh[B][1]}), pf[0],
+        oacc[B][0], 0, 0, 0),
+    oacc[B][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, (u32x4){vl[B][0], vl[B][1], vh[B][0], vh[B][1]}), pf[1],
+        oacc[B][1], 0, 0, 0),
+    vl[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B)>(addr),
+    vh[B] = lds_read_tr16_at<64 * (4 * VCH * C + 4 * B) + 128 * VCH>(addr)),
+   ...);
+}
 template <int OFF>
 __device__ inline u32x4 lds_read_b128_at(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset");
@@ -847,8 +865,9 @@ struct SplitCfg {
 //                 S(i - 1), which go to LDS as P(i - 1) (bf16, already in the
 //                 B-operand layout of the PV product: lane l of the output
 //                 wave reads what lane l of its score wave wrote);
-//   output waves: O^T += V(i - 3)^T P(i - 3)^T from registers, then the reads
-//                 of V(i - 2) and P(i - 2) for the next iteration.
+//   output waves: O^T += V(i - 3)^T P(i - 3)^T from registers, each operand
+//                 register reloaded with its part of V(i - 2) or P(i - 2) for
+//                 the next iteration right after its last product.
 // The arithmetic and its order are those of attn_fwd_bf16_kernel<.., 2, false>
 // (same scores, same bf16 probabilities, same row sums, same product order),
 // so outputs, log-sum-exps and flags are bitwise the same; the exact pass of
@@ -941,15 +960,20 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   const uint32_t v_lane =
       (uint32_t)(4 * ((lane >> 2) / VCH) + (lane & 3)) * v_rb + (uint32_t)((lane >> 2) % VCH) * 16u;
   // Who copies a tile: at qk 192 the score waves copy K (and the key
-  // positions) right after the barrier and the output waves V after their
-  // products; at qk 128 the score waves copy the whole tile right after the
-  // barrier (measured: 2-3 % faster there, no faster at qk 192)
-  constexpr bool S_ALL = DQK == 128;
+  // positions), the output waves V; at qk 128 the output waves copy the whole
+  // tile.  The output waves issue theirs after their products; the score
+  // waves, theirs right after the barrier or among their products.  (With
+  // the output waves' reads running among their products, the score waves'
+  // path is the longer one; handing them no copies at qk 192 measured 2 %
+  // slower, on the 8192-token shards at qk 128 about 3 % faster.)
+  constexpr bool K_S = DQK != 128;  // K and the key positions: score waves
+  constexpr bool V_S = false;       // V: output waves
+  constexpr bool O_DMA = !K_S || !V_S;
   auto issue = [&](int t) {
     const int j0 = t * BN;
     const int nrows = min(BN, n_kv - j0);
     u32x4 *dst = sm[t % NBUF];
-    if (score) {
+    if (score == K_S) {
       const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(kbase + (int64_t)j0 * p.k_rs), (short)0, (int)(nrows * k_rb), 0x00020000);
 #pragma unroll
@@ -967,7 +991,7 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
             0, 0, 0);
       }
     }
-    if (score == S_ALL) {
+    if (score == V_S) {
       const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(vbase + (int64_t)j0 * p.v_rs), (short)0, (int)(nrows * v_rb), 0x00020000);
 #pragma unroll
@@ -983,18 +1007,22 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
   // iteration i begins: this wave's part of tile i has landed and its LDS
   // operations of iteration i - 1 are done; after the barrier every wave has
   // all of tile i and P(i - 2) of every score wave.  The score waves then
-  // issue their part of tile i + PREF; the output waves issue theirs (qk 192)
-  // after their products, which then start sooner (2-3 % faster)
+  // issue their part of tile i + PREF; the output waves issue theirs after
+  // their products, which then start sooner (2-3 % faster)
   // (s_dma = false: a score wave in its steady-state loop issues the copy
   // inside its fused block instead, among the products: 0.5-2 % faster)
   auto top = [&](int i, bool s_dma = true) {
     const int later = min(n_wg - 1 - i, PREF - 1);
-    constexpr int SPER = C::KDMA + (S_ALL ? C::VDMA : 0);  // score wave's DMA per tile
+    // copy instructions per tile of a score and of an output wave (wave 0 of
+    // the K role also copies the key positions)
+    constexpr int SPER = (K_S ? C::KDMA : 0) + (V_S ? C::VDMA : 0);
+    constexpr int OPER = (K_S ? 0 : C::KDMA) + (V_S ? 0 : C::VDMA);
     if (score) {
-      if (kvp && s == 0) wait_later_lgkm0<SPER + 1, PREF - 1>(later);
+      if (K_S && kvp && s == 0) wait_later_lgkm0<SPER + 1, PREF - 1>(later);
       else wait_later_lgkm0<SPER, PREF - 1>(later);
     } else {
-      wait_later_lgkm0<S_ALL ? 0 : C::VDMA, PREF - 1>(later);
+      if (!K_S && kvp && s == 0) wait_later_lgkm0<OPER + 1, PREF - 1>(later);
+      else wait_later_lgkm0<OPER, PREF - 1>(later);
     }
     __builtin_amdgcn_s_barrier();
     if (score && s_dma && i + PREF < n_wg) issue(i + PREF);
@@ -1201,12 +1229,13 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
         oacc[b][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb], oacc[b][rb], 0, 0, 0);
     }
   };
-  // Iteration i multiplies P(i - 3) and V(i - 3), read into registers at the
-  // end of iteration i - 1 (both were complete at its barrier), so the
-  // products start right after the barrier instead of behind the burst of
-  // LDS reads every wave issues there; then it reads P(i - 2) and V(i - 2)
-  // for the next iteration (complete at the next barrier: top() waits for
-  // this wave's LDS operations).
+  // Iteration i multiplies P(i - 3) and V(i - 3), read into registers during
+  // iteration i - 1 (both were complete at its barrier), so the products
+  // start right after the barrier instead of behind the burst of LDS reads
+  // every wave issues there; meanwhile it reads P(i - 2) and V(i - 2) for
+  // the next iteration (complete at the next barrier: top() waits for this
+  // wave's LDS operations).  pv_reads and pv_products are the pipeline's
+  // fill and drain; pv_products_reload below is its steady state.
   const uint32_t pr_lds = lds_u32(&pbuf[0][s][0][lane]);
   static_assert(RB == 2, "P layout");
   u32x4 q00, q01, q10, q11;
@@ -1234,11 +1263,51 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
     pv_mma(vl0, vh0, pf0);
     pv_mma(vl1, vh1, pf1);
   };
-  for (int i = 0; i < n_wg + 2; ++i) {
+  // the steady state: the products of tile u - 1 with every operand register
+  // reloaded from tile u right after its last product (tile u and P(u) are
+  // complete at this iteration's barrier)
+  auto pv_products_reload = [&](int u, int i) {
+    lds_wait_later<0>(vl0, vh0);
+    lds_wait_later<0>(vl1, vh1);
+    lds_wait_tie<0>(q00);
+    lds_wait_tie<0>(q01);
+    lds_wait_tie<0>(q10);
+    lds_wait_tie<0>(q11);
+    const uint32_t pr = pr_lds + (uint32_t)((u & 1) * 4 * 2 * RB * 64 * 16);
+    const uint32_t va = lds_u32(stage(u)) + (uint32_t)vt;
+    {
+      const bf16x8 pf0[RB] = {__builtin_bit_cast(bf16x8, q00), __builtin_bit_cast(bf16x8, q10)};
+      reload_mma<VCH, OB, 0>(va, vl0, vh0, pf0, oacc, std::make_integer_sequence<int, OB>{});
+    }
+    q00 = lds_read_b128_at<0 * 1024>(pr);
+    q10 = lds_read_b128_at<2 * 1024>(pr);
+    {
+      const bf16x8 pf1[RB] = {__builtin_bit_cast(bf16x8, q01), __builtin_bit_cast(bf16x8, q11)};
+      reload_mma<VCH, OB, 1>(va, vl1, vh1, pf1, oacc, std::make_integer_sequence<int, OB>{});
+    }
+    q01 = lds_read_b128_at<1 * 1024>(pr);
+    q11 = lds_read_b128_at<3 * 1024>(pr);
+    // the copy after the products: 1 % faster than between the two key
+    // steps, 2 % faster than before the products (qk 192)
+    if (O_DMA && i + PREF < n_wg) issue(i + PREF);
+  };
+  // Three loops, so that the steady state's body has no branch: with one,
+  // the register allocator gave its two paths different homes for the
+  // accumulators and spilled them (120-320 registers) at the join.
+  int i = 0;
+  for (; i < 3 && i < n_wg + 2; ++i) {
     top(i);
-    if (i >= 3 && i - 3 < n_vis) pv_products();
-    if (!S_ALL && i + PREF < n_wg) issue(i + PREF);
-    if (i >= 2 && i - 2 < n_vis) pv_reads(i - 2);
+    if (O_DMA && i + PREF < n_wg) issue(i + PREF);
+    if (i == 2 && n_vis > 0) pv_reads(0);
+  }
+  for (; i <= n_vis + 1; ++i) {  // the products of tile i - 3, the reads of tile i - 2
+    top(i);
+    pv_products_reload(i - 2, i);
+  }
+  for (; i < n_wg + 2; ++i) {
+    top(i);
+    if (i - 3 < n_vis) pv_products();
+    if (O_DMA && i + PREF < n_wg) issue(i + PREF);
   }
   if (n_wg >= 1 && n_wg - 1 < n_vis) {  // the last tile, read in the last iteration
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
