@@ -1071,7 +1071,9 @@ void attn_fwd_bf16_split_kernel(const AttnParams p, const LaunchSegs L) {
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[rb][i] = 0.f;
-      constexpr int KLA = KS < 4 ? KS : 4;
+      // K fragment reads in flight: six at qk 192 (1.3 % faster than four
+      // since the output waves' reads run among their products), four at qk 128
+      constexpr int KLA = DQK == 192 ? 6 : (KS < 4 ? KS : 4);
       const uint32_t ka = kq_lds + (uint32_t)((t % NBUF) * C::STAGE * 16);
       bf16x8 kf[KLA];
       split_k_first<0, KLA>(ka, kf);
