@@ -846,9 +846,12 @@ struct SplitCfg {
   using C = Cfg<DQK, DV>;
   static constexpr int PBYTES = 2 * 4 * 4096;
   static constexpr int NBUF_FIT = (160 * 1024 - PBYTES - 3 * 1024) / (C::STAGE * 16);
-  // five stages, two tiles in flight beyond the three being read: measured
-  // faster than six to eight (0.5 % at qk 192, 3-4 % at qk 128)
-  static constexpr int NBUF = NBUF_FIT < 5 ? NBUF_FIT : 5;
+  // at qk 192 five stages, two tiles in flight beyond the three being read:
+  // measured faster than six or seven; at qk 128 six (since the output
+  // waves copy whole tiles after their products: 1 % faster than five on the
+  // 12-request interleave, seven slower)
+  static constexpr int NBUF_MAX = DQK == 128 ? 6 : 5;
+  static constexpr int NBUF = NBUF_FIT < NBUF_MAX ? NBUF_FIT : NBUF_MAX;
   // a stage is read in iterations i (K) and i + 2 (V)
   static constexpr int PREF = NBUF - 3;
   static_assert(PREF >= 2, "stages");
