@@ -42,7 +42,8 @@
 // For qk 192 (the MLA shape) and qk 128 the main pass of 256-row workgroups runs
 // as attn_fwd_bf16_split_kernel instead: 8 waves, two per SIMD, the score waves
 // holding Q and the output waves holding O of the same 64 rows, with the
-// probabilities handed over through LDS (five stages, two tiles in flight).
+// probabilities handed over through LDS (five stages at qk 192, six at qk
+// 128).
 // A single wave per SIMD issues its products, exponentials, DMA descriptors
 // and waits in order and leaves the matrix core idle whenever it stalls; with
 // two waves per SIMD the other wave's products fill those gaps.  Same
