@@ -848,7 +848,7 @@ struct SplitCfg {
   static constexpr int PBYTES = 2 * 4 * 4096;
   static constexpr int NBUF_FIT = (160 * 1024 - PBYTES - 3 * 1024) / (C::STAGE * 16);
   // at qk 192 five stages, two tiles in flight beyond the three being read:
-  // measured faster than six or seven; at qk 128 six (since the output
+  // measured faster than the six that fit; at qk 128 six (since the output
   // waves copy whole tiles after their products: 1 % faster than five on the
   // 12-request interleave, seven slower)
   static constexpr int NBUF_MAX = DQK == 128 ? 6 : 5;
